@@ -1,0 +1,136 @@
+/*
+ * ssa.h - C ABI of the Skip-Softmax (BLASST) FlashAttention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every (batch, head) and every query row i the library
+ * computes softmax attention O_i = sum_c p_ic v_c with
+ * p_ic = exp(s_ic) / sum exp(s_ic), s_ic = scale * (q_i . k_c), in one
+ * streaming pass over key tiles of 128 keys ("Skip-Softmax" page of the
+ * vLLM-Omni documentation, section "The online-softmax pass"), with the
+ * BLASST skip test in front of each tile ("Skip-Softmax" design document of
+ * vLLM-Omni, section "Algorithm"): for a block of 64 query rows and a key
+ * tile, with tile_max[i] the row's largest score in the tile and m[i] the
+ * row's running maximum over the tiles absorbed so far, the tile is skipped
+ * when tile_max[i] - m[i] < ln(lambda) holds for every row of the block
+ * (strict '<'); a skipped tile's exponentials and P.V product are never
+ * computed and it contributes nothing to the row sums.  The scores QK^T are
+ * always computed.  lambda = 0 disables the test and gives dense attention.
+ *
+ * The threshold (design document, section "From configuration to the kernel
+ * threshold"; documentation, section "The threshold"):
+ *   ssa_fwd             lambda = factor / seqlen
+ *   ssa_fwd_threshold   lambda = threshold (the direct control: independent
+ *                       of the sequence length)
+ *   ssa_fwd_calibrated  lambda = a * exp(b * target_sparsity) / seqlen (the
+ *                       calibrated control; only this curve is accepted)
+ * ln(lambda) is evaluated once on the host in double precision and rounded
+ * to float; the per-tile comparison runs in float.
+ *
+ * Tiles: 64 query rows x 128 keys, keys visited in ascending order from 0.
+ * A last query block shorter than 64 rows votes with its valid rows only;
+ * a last key tile shorter than 128 keys is padded with keys of score -inf.
+ *
+ * Layouts and ownership (all buffers are device memory owned by the caller;
+ * the library allocates nothing, never synchronises, and enqueues one kernel
+ * on `stream`, a hipStream_t or NULL for the default stream):
+ *   q, k, v, o    bf16, [B, H, S, D] contiguous, 16-byte aligned, D = 128.
+ *   lse           float [B, H, S]: LSE_i = m_i + ln(l_i), natural log of the
+ *                 row's softmax denominator over the kept tiles. May be NULL.
+ *   skip_counts   int32 [B, H, ceil(S/64)]: number of skipped key tiles of
+ *                 each 64-row query block. May be NULL.
+ * Inputs o, lse and skip_counts are overwritten; q, k, v are read only.
+ *
+ * Errors.  Every argument is checked on the host before any HIP call; a bad
+ * call returns a negative ssa_status and enqueues nothing.  On a device that
+ * is not gfx950 every entry point returns SSA_ERR_DEVICE (no fallback).  A
+ * failed launch returns SSA_ERR_LAUNCH.  ssa_strerror() names the code and
+ * ssa_last_error() returns a message about the last failure of the calling
+ * thread.  B, H or S equal to 0 is a valid empty call that returns SSA_OK.
+ */
+#ifndef SSA_H_
+#define SSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSA_OK = 0,
+  SSA_ERR_INVALID_ARG = -1,    /* null or misaligned pointer, negative size, non-finite scale */
+  SSA_ERR_UNSUPPORTED = -2,    /* head dimension other than 128, sizes beyond the grid limits */
+  SSA_ERR_BAD_THRESHOLD = -3,  /* factor / threshold / lambda negative or non-finite, seqlen <= 0 */
+  SSA_ERR_NO_CALIBRATION = -4, /* calibrated call with a <= 0 or non-finite a, b: use the threshold entry */
+  SSA_ERR_DEVICE = -5,         /* no HIP device, or the current device is not gfx950 */
+  SSA_ERR_LAUNCH = -6          /* the kernel launch failed */
+} ssa_status;
+
+/* Threshold controls of ssa_fwd_varlen and ssa_resolve_threshold. */
+typedef enum {
+  SSA_MODE_FACTOR = 0,     /* p0 = factor: lambda_b = factor / S_b                     */
+  SSA_MODE_THRESHOLD = 1,  /* p0 = threshold: lambda_b = threshold                     */
+  SSA_MODE_CALIBRATED = 2  /* p0 = a, p1 = b, p2 = target_sparsity:
+                              lambda_b = a * exp(b * target_sparsity) / S_b            */
+} ssa_mode;
+
+#define SSA_HEAD_DIM 128
+#define SSA_BLOCK_Q 64
+#define SSA_BLOCK_K 128
+
+/* lambda = factor / seqlen.  factor >= 0 and finite, seqlen > 0 (normally S). */
+int ssa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int S, int D, float scale, float factor, int seqlen,
+            int32_t* skip_counts, void* stream);
+
+/* lambda = threshold.  threshold >= 0 and finite; values above 1 are accepted. */
+int ssa_fwd_threshold(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int S, int D, float scale, float threshold,
+                      int32_t* skip_counts, void* stream);
+
+/* lambda = a * exp(b * target_sparsity) / seqlen.  a > 0, a and b finite
+ * (else SSA_ERR_NO_CALIBRATION), target_sparsity finite, seqlen > 0. */
+int ssa_fwd_calibrated(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int S, int D, float scale, float a, float b,
+                       float target_sparsity, int seqlen, int32_t* skip_counts, void* stream);
+
+/* Packed variable-length batch ("cu_seqlens" layout): sequence b holds the
+ * tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, k, v, o, which are bf16
+ * [T, H, D] with T = cu_seqlens[nseq].  cu_seqlens: device int32 [nseq + 1],
+ * non-decreasing from 0; every length must be <= max_seqlen.  Attention never
+ * crosses sequences and each sequence normalises lambda by its own length
+ * S_b (see ssa_mode).  lse: float [H, T] (nullable).  skip_counts: int32
+ * [H, sum_b ceil(S_b / 64)], query blocks of sequence b after those of
+ * sequences 0..b-1 (nullable). */
+int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int32_t* cu_seqlens, int nseq, int max_seqlen, int H, int D,
+                   float scale, int mode, double p0, double p1, double p2,
+                   int32_t* skip_counts, void* stream);
+
+/* Any of the three controls (see ssa_mode; S_b = seqlen) with every tile
+ * decision reported: tile_mask uint8 [B, H, ceil(S/64), ceil(S/128)]
+ * (1 = skipped) and tile_margin float (same shape, nullable): the largest
+ * tile_max[i] - m[i] over the block's valid rows, +inf on the first tile.
+ * Same arithmetic as the other entry points. */
+int ssa_fwd_debug(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int S, int D, float scale, int mode, double p0, double p1,
+                  double p2, int seqlen, int32_t* skip_counts, uint8_t* tile_mask,
+                  float* tile_margin, void* stream);
+
+/* Host-only: the ln(lambda) the kernels compare against for one sequence of
+ * length seqlen, and whether the test is on (lambda > 0).  No HIP call. */
+int ssa_resolve_threshold(int mode, double p0, double p1, double p2, int seqlen,
+                          float* ln_lambda, int* vote_enabled);
+
+/* SSA_OK when the current HIP device is gfx950. */
+int ssa_device_check(void);
+
+const char* ssa_strerror(int status);
+const char* ssa_last_error(void);
+int ssa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H_ */

@@ -1,0 +1,218 @@
+"""Skip-Softmax (BLASST) FlashAttention forward on AMD Instinct MI355X.
+
+Thin ctypes binding of the C ABI in include/ssa.h (libssa.so, built for
+gfx950).  This module only marshals arguments: it checks tensor dtypes,
+shapes and devices, allocates the outputs with torch, and passes raw device
+pointers and the current HIP stream to the library, which enqueues one
+kernel.  Every step of the attention runs in the HIP kernel; there is no
+fallback.  If libssa.so is missing or the device is not gfx950 the calls
+raise.
+
+Controls ("Skip-Softmax" design document of vLLM-Omni, section "From
+configuration to the kernel threshold"), exactly one per call:
+  factor=f           lambda = f / seqlen      (the kernel's own input)
+  threshold=t        lambda = t               (direct control)
+  calib=(a, b, s)    lambda = a exp(b s) / seqlen   (calibrated control)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "SsaError", "fwd", "fwd_varlen", "fwd_debug", "resolve_threshold", "device_check",
+    "library_path", "load_library", "BLOCK_Q", "BLOCK_K", "HEAD_DIM",
+    "MODE_FACTOR", "MODE_THRESHOLD", "MODE_CALIBRATED",
+]
+
+HEAD_DIM = 128
+BLOCK_Q = 64
+BLOCK_K = 128
+MODE_FACTOR, MODE_THRESHOLD, MODE_CALIBRATED = 0, 1, 2
+
+SSA_OK = 0
+STATUS_NAMES = {
+    0: "SSA_OK", -1: "SSA_ERR_INVALID_ARG", -2: "SSA_ERR_UNSUPPORTED", -3: "SSA_ERR_BAD_THRESHOLD",
+    -4: "SSA_ERR_NO_CALIBRATION", -5: "SSA_ERR_DEVICE", -6: "SSA_ERR_LAUNCH",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class SsaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "_lib", "libssa.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libssa.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -m skip_softmax_flashattention_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I, F, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    lib.ssa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, F, I, P, P]
+    lib.ssa_fwd_threshold.argtypes = [P, P, P, P, P, I, I, I, I, F, F, P, P]
+    lib.ssa_fwd_calibrated.argtypes = [P, P, P, P, P, I, I, I, I, F, F, F, F, I, P, P]
+    lib.ssa_fwd_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, D, D, D, P, P]
+    lib.ssa_fwd_debug.argtypes = [P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, P, P]
+    lib.ssa_resolve_threshold.argtypes = [I, D, D, D, I, ctypes.POINTER(F), ctypes.POINTER(I)]
+    for name in ("ssa_fwd", "ssa_fwd_threshold", "ssa_fwd_calibrated", "ssa_fwd_varlen", "ssa_fwd_debug",
+                 "ssa_resolve_threshold", "ssa_device_check", "ssa_version"):
+        getattr(lib, name).restype = I
+    lib.ssa_device_check.argtypes = []
+    lib.ssa_version.argtypes = []
+    lib.ssa_strerror.argtypes = [I]
+    lib.ssa_strerror.restype = ctypes.c_char_p
+    lib.ssa_last_error.argtypes = []
+    lib.ssa_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(code: int) -> None:
+    if code != SSA_OK:
+        lib = load_library()
+        raise SsaError(code, lib.ssa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _control(factor, threshold, calib) -> Tuple[int, float, float, float]:
+    given = [x is not None for x in (factor, threshold, calib)]
+    if sum(given) != 1:
+        raise ValueError("give exactly one of factor=, threshold= or calib=(a, b, target_sparsity)")
+    if factor is not None:
+        return MODE_FACTOR, float(factor), 0.0, 0.0
+    if threshold is not None:
+        return MODE_THRESHOLD, float(threshold), 0.0, 0.0
+    a, b, s = calib
+    return MODE_CALIBRATED, float(a), float(b), float(s)
+
+
+def _check_qkv(q, k, v, ndim):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if t.dim() != ndim or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+        factor: Optional[float] = None, threshold: Optional[float] = None, calib=None,
+        seqlen: Optional[int] = None, with_lse: bool = True, with_counts: bool = True,
+        out: Optional[torch.Tensor] = None):
+    """Skip-softmax attention of bf16 [B, H, S, 128] tensors.
+
+    Returns (o, lse, skip_counts): o bf16 [B, H, S, 128], lse float32
+    [B, H, S] (or None), skip_counts int32 [B, H, ceil(S/64)] (or None).
+    ``seqlen`` (the length lambda is normalised by) defaults to S.
+    """
+    _check_qkv(q, k, v, 4)
+    B, H, S, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    mode, p0, p1, p2 = _control(factor, threshold, calib)
+    n = S if seqlen is None else int(seqlen)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if with_lse else None
+    cnt = torch.empty((B, H, -(-S // BLOCK_Q)), dtype=torch.int32, device=q.device) if with_counts else None
+    lib = load_library()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, scale)
+    if mode == MODE_FACTOR:
+        rc = lib.ssa_fwd(*args, p0, n, _ptr(cnt), _stream(q))
+    elif mode == MODE_THRESHOLD:
+        rc = lib.ssa_fwd_threshold(*args, p0, _ptr(cnt), _stream(q))
+    else:
+        rc = lib.ssa_fwd_calibrated(*args, p0, p1, p2, n, _ptr(cnt), _stream(q))
+    _check(rc)
+    return o, lse, cnt
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+               max_seqlen: int, *, scale: Optional[float] = None, factor: Optional[float] = None,
+               threshold: Optional[float] = None, calib=None, with_lse: bool = True,
+               with_counts: bool = True):
+    """Packed variable-length batch: q, k, v bf16 [T, H, 128], cu_seqlens int32
+    [nseq + 1] on the device.  Each sequence normalises lambda by its own
+    length.  Returns (o [T, H, 128], lse [H, T], skip_counts [H, sum ceil(S_b/64)])."""
+    _check_qkv(q, k, v, 3)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be an int32 1-D tensor on the same device as q")
+    T, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    mode, p0, p1, p2 = _control(factor, threshold, calib)
+    nseq = cu_seqlens.numel() - 1
+    lens = (cu_seqlens[1:] - cu_seqlens[:-1]).tolist() if with_counts else []
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if with_lse else None
+    cnt = None
+    if with_counts:
+        cnt = torch.empty((H, sum(-(-n // BLOCK_Q) for n in lens)), dtype=torch.int32, device=q.device)
+    lib = load_library()
+    rc = lib.ssa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), nseq,
+                            int(max_seqlen), H, D, scale, mode, p0, p1, p2, _ptr(cnt), _stream(q))
+    _check(rc)
+    return o, lse, cnt
+
+
+def fwd_debug(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+              factor: Optional[float] = None, threshold: Optional[float] = None, calib=None,
+              seqlen: Optional[int] = None):
+    """fwd with every tile decision: returns (o, lse, skip_counts, tile_mask
+    uint8 [B, H, nQB, nKT] (1 = skipped), tile_margin float32 [B, H, nQB, nKT])."""
+    _check_qkv(q, k, v, 4)
+    B, H, S, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    mode, p0, p1, p2 = _control(factor, threshold, calib)
+    n = S if seqlen is None else int(seqlen)
+    nqb, nkt = -(-S // BLOCK_Q), -(-S // BLOCK_K)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    cnt = torch.empty((B, H, nqb), dtype=torch.int32, device=q.device)
+    mask = torch.empty((B, H, nqb, nkt), dtype=torch.uint8, device=q.device)
+    margin = torch.empty((B, H, nqb, nkt), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    rc = lib.ssa_fwd_debug(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, scale, mode, p0, p1, p2, n,
+                           _ptr(cnt), _ptr(mask), _ptr(margin), _stream(q))
+    _check(rc)
+    return o, lse, cnt, mask, margin
+
+
+def resolve_threshold(mode: int, p0: float, p1: float = 0.0, p2: float = 0.0, seqlen: int = 1):
+    """Host-only: (ln_lambda as float32, vote enabled) as the library computes them."""
+    lib = load_library()
+    ln = ctypes.c_float()
+    on = ctypes.c_int()
+    _check(lib.ssa_resolve_threshold(int(mode), float(p0), float(p1), float(p2), int(seqlen),
+                                     ctypes.byref(ln), ctypes.byref(on)))
+    return ln.value, bool(on.value)
+
+
+def device_check() -> None:
+    """Raise SsaError unless the current HIP device is gfx950."""
+    _check(load_library().ssa_device_check())

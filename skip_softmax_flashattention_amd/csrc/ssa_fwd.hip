@@ -1,0 +1,663 @@
+// Skip-Softmax (BLASST) FlashAttention forward for AMD Instinct MI355X (gfx950).
+//
+// The method: "Skip-Softmax" design document of vLLM-Omni, section
+// "Algorithm"; "Skip-Softmax" page of the vLLM-Omni documentation, sections
+// "The online-softmax pass" and "The skip test".  The C ABI is declared in
+// include/ssa.h.
+//
+// Work decomposition.  One workgroup = 4 waves = 256 query rows of one
+// (sequence, head).  Each wave owns one 64-row query block, which is exactly
+// one vote group of the skip test, so the all-rows vote is a single wave
+// ballot with no cross-wave traffic.  Key tiles of 128 keys stream through
+// LDS, double buffered, shared by the four waves.  Tiles are copied from
+// global memory straight into LDS (buffer loads with the LDS-destination
+// bit), so staging costs no registers; keys past the end of the sequence lie
+// outside the buffer resource's range and arrive as zeros.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  A wave
+// computes the transposed score tile S^T = K Q^T as 4 key sub-blocks x 2
+// query sub-blocks of 32 x 32.  In the 32x32 accumulator layout a lane holds
+// one query column and 16 key rows, so each lane owns two query rows (c and
+// 32 + c) and 64 of the tile's 128 keys: the row maximum and row sum are
+// in-lane reductions plus one exchange between the two wave halves.  The key
+// rows of the K operand are permuted so that a lane's accumulator registers
+// 8t..8t+7 hold 8 *consecutive* keys; rounded to bf16 they are directly the
+// B operand (P^T) of O^T = V^T P^T.  The A operand V^T comes from the
+// natural-layout V tile through two LDS transpose reads (ds_read_b64_tr_b16).
+//
+// The skip test runs on fp32 scores in log space before any exponential:
+// tile_max[i] - m[i] < ln(lambda) for every valid row of the wave's block,
+// m the true running maximum over the kept tiles.  A skipped tile costs only
+// its QK^T and row maximum; m, l and O are left untouched.
+//
+// Exponent reference.  The exponentials use a per-row reference r <= m and
+// O, l are rescaled only when m climbs more than kRescaleLog2 binades above
+// r (then r = m).  This changes only rounding: O / l and r + ln(l) are
+// independent of the reference.  P = exp(s - r) stays below 2^kRescaleLog2.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "ssa.h"
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBQ = 64;                 // query rows per wave = rows per vote group
+constexpr int kBK = 128;                // keys per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWG = kBQ * kWaves;
+constexpr int kRowBytes = kD * 2;                  // one bf16 row of 128 channels
+constexpr int kTileBytes = kBK * kRowBytes;        // 32 KB
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 10.f;               // P <= 2^10 before a rescale is forced
+constexpr unsigned kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int32_t* counts;
+  uint8_t* mask;
+  float* margin;
+  const int32_t* cu_seqlens;   // null: fixed-length [B, H, S, D]
+  int nseq;                    // B
+  int H;
+  int S;                       // fixed length, or max_seqlen
+  int qgroups;                 // workgroups per (sequence, head)
+  long long tok_stride;        // elements between consecutive tokens
+  long long head_stride;       // elements between heads
+  long long seq_stride;        // elements between batch entries (fixed length)
+  float scale;
+  float scale_log2e;
+  float ln_lambda;             // used when lambda_per_seq == 0
+  int vote;                    // 0: lambda == 0, nothing is skipped
+  int lambda_per_seq;          // 1: ln(lambda_b) = ln(factor / S_b)
+  double factor;
+};
+
+// XOR swizzle of the 16-byte chunk index within a 256-byte LDS row, a linear
+// map of the row's low 4 bits.  It makes the 16-byte K operand reads (rows
+// permuted by key_perm) and the transpose reads of V hit distinct banks for
+// every group of 8 and of 16 lanes; whole-row writes are unaffected.
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
+}
+
+// Key row that MFMA row m (0..31) of a 32-key sub-block loads.  With this
+// permutation accumulator register r of lane half hf holds key
+// 16 * (r / 8) + 8 * hf + (r % 8) of the sub-block.
+__device__ __forceinline__ int key_perm(int m) {
+  const int a = m >> 3, hh = (m >> 2) & 1, j = m & 3;
+  return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + j;
+}
+
+// Both halves of the wave receive f(x[lane], x[lane ^ 32]).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
+}
+
+template <bool kDebug>
+__global__ __launch_bounds__(kThreads, 1) void ssa_fwd_kernel(const Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
+
+  const int qg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, hf = lane >> 5;
+
+  long long tok0 = 0;
+  int S_b = p.S;
+  if (p.cu_seqlens != nullptr) {
+    tok0 = p.cu_seqlens[b];
+    S_b = p.cu_seqlens[b + 1] - (int)tok0;
+  }
+  if (qg * kRowsPerWG >= S_b) return;   // whole workgroup past the end of its sequence
+
+  const long long base = (p.cu_seqlens != nullptr ? tok0 * p.tok_stride : (long long)b * p.seq_stride) +
+                         (long long)h * p.head_stride;
+  const uint32_t ts_bytes = (uint32_t)(p.tok_stride * 2);
+  // Byte range of this (sequence, head): its last token's row ends the range.
+  const uint32_t range = (uint32_t)((long long)(S_b - 1) * p.tok_stride * 2 + kRowBytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, range);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, range);
+
+  float ln_lambda = p.ln_lambda;
+  if (p.lambda_per_seq) ln_lambda = (float)log(p.factor / (double)S_b);
+  const bool vote = p.vote != 0;
+
+  const int nkt = (S_b + kBK - 1) / kBK;
+  const int qb = qg * kWaves + wave;
+  const int wrow0 = qb * kBQ;
+  const bool wave_active = wrow0 < S_b;
+  const bool valid0 = wrow0 + c < S_b;
+  const bool valid1 = wrow0 + 32 + c < S_b;
+
+  // Q^T operand fragments: qf[qs][s] = Q[wrow0 + 32 qs + c][16 s + 8 hf .. +7]
+  // (rows past the end read as zeros).
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const uint32_t off = (uint32_t)(wrow0 + 32 * qs + c) * ts_bytes + 16u * hf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[qs][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32u * s, 0, 0));
+  }
+
+  // ---- tile copy: global -> LDS, 16 bytes per lane per instruction ----
+  // Instruction j of wave w fills LDS rows 32 w + 4 j .. +3 (1 KB); lane l
+  // lands at byte 16 l of that block: row 32 w + 4 j + l / 16, physical
+  // chunk l % 16, which holds logical chunk (l % 16) ^ swz(row).
+  uint32_t copy_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 32 * wave + 4 * j + (lane >> 4);
+    copy_off[j] = (uint32_t)r * ts_bytes + 16u * (uint32_t)((lane & 15) ^ swz(r));
+  }
+  auto issue_tile = [&](int kt, unsigned char* kdst, unsigned char* vdst) {
+    const uint32_t tile_off = (uint32_t)kt * kBK * ts_bytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = (32 * wave + 4 * j) * kRowBytes;
+      // The whole offset goes in the per-lane (range-checked) voffset.
+      const uint32_t off = copy_off[j] + tile_off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(void, kdst + blk), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(void, vdst + blk), 16, off, 0, 0, 0);
+    }
+  };
+
+  // Per-lane LDS byte offsets of the operand reads.
+  // K operand (A of S^T): row 32 kb + key_perm(c), logical chunk 2 s + hf.
+  const int krow = key_perm(c);
+  const int kswz = swz(krow);
+  // V^T operand (A of O^T) via transpose reads: within 16-lane group g the
+  // lane 4 e + q supplies row 8 hf + 4 ih + e (plus the 16-key step base),
+  // channels 32 db + 16 (g % 2) + 4 q .. +3.
+  const int ve = (lane & 15) >> 2, vq = lane & 3, vg = (lane >> 4) & 1;
+  int voff[2][4];
+#pragma unroll
+  for (int ih = 0; ih < 2; ++ih) {
+    const int row = 8 * hf + 4 * ih + ve;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int lc = 4 * db + 2 * vg + (vq >> 1);
+      voff[ih][db] = row * kRowBytes + 16 * (lc ^ swz(row)) + 8 * (vq & 1);
+    }
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max (natural units), drives the vote
+  float mb_ref[2] = {-INFINITY, -INFINITY};  // exponent reference, log2 units
+  float l[2] = {0.f, 0.f};
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][qs][r] = 0.f;
+  int nskip = 0;
+
+  auto compute_tile = [&](int kt, const unsigned char* kl, const unsigned char* vl) {
+    // ---- scores S^T = K Q^T (always computed) ----
+    f32x16 sacc[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][qs][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int koff = krow * kRowBytes + 16 * ((2 * s + hf) ^ kswz);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + kb * 32 * kRowBytes + koff));
+        sacc[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][s], sacc[kb][0], 0, 0, 0);
+        sacc[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][s], sacc[kb][1], 0, 0, 0);
+      }
+    }
+    // Keys past the end of the sequence score -inf.
+    if ((kt + 1) * kBK > S_b) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * kBK + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);
+          if (key >= S_b) {
+            sacc[kb][0][r] = -INFINITY;
+            sacc[kb][1][r] = -INFINITY;
+          }
+        }
+    }
+
+    // ---- tile maximum per query row and the skip vote ----
+    float tmax[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float mx = sacc[0][qs][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qs][r]);
+      tmax[qs] = halves_max(mx) * p.scale;
+    }
+    const float d0 = tmax[0] - m_run[0];
+    const float d1 = tmax[1] - m_run[1];
+    const bool pass = (!valid0 || d0 < ln_lambda) && (!valid1 || d1 < ln_lambda);
+    const bool skip = vote && (__builtin_amdgcn_ballot_w64(!pass) == 0);
+
+    if constexpr (kDebug) {
+      float md = fmaxf(valid0 ? d0 : -INFINITY, valid1 ? d1 : -INFINITY);
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) md = fmaxf(md, __shfl_xor(md, off));
+      if (lane == 0) {
+        const long long nqb = (S_b + kBQ - 1) / kBQ;
+        const long long idx = (((long long)b * p.H + h) * nqb + qb) * nkt + kt;
+        if (p.mask != nullptr) p.mask[idx] = skip ? 1 : 0;
+        if (p.margin != nullptr) p.margin[idx] = md;
+      }
+    }
+
+    if (skip) {
+      ++nskip;
+      return;
+    }
+
+    // ---- kept tile: online-softmax update ----
+    bool grow = false;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      m_run[qs] = fmaxf(m_run[qs], tmax[qs]);
+      grow |= m_run[qs] * kLog2e > mb_ref[qs] + kRescaleLog2;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const float nb = m_run[qs] * kLog2e;
+        const float alpha = __builtin_amdgcn_exp2f(mb_ref[qs] - nb);   // 0 on the first kept tile
+        mb_ref[qs] = nb;
+        l[qs] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][qs][r] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qs][r], p.scale_log2e, -mb_ref[qs]));
+          sacc[kb][qs][r] = e;
+          rs += e;
+        }
+      l[qs] += rs;
+    }
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        u32x4 p0, p1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          p0[w] = pack_bf16(sacc[kb][0][8 * t2 + 2 * w], sacc[kb][0][8 * t2 + 2 * w + 1]);
+          p1[w] = pack_bf16(sacc[kb][1][8 * t2 + 2 * w], sacc[kb][1][8 * t2 + 2 * w + 1]);
+        }
+        const bf16x8 pf0 = __builtin_bit_cast(bf16x8, p0), pf1 = __builtin_bit_cast(bf16x8, p1);
+        const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
+          u32x4 av;
+          av[0] = __builtin_bit_cast(u32x2, lo)[0];
+          av[1] = __builtin_bit_cast(u32x2, lo)[1];
+          av[2] = __builtin_bit_cast(u32x2, hi)[0];
+          av[3] = __builtin_bit_cast(u32x2, hi)[1];
+          const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+          oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf0, oacc[db][0], 0, 0, 0);
+          oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf1, oacc[db][1], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- main loop: two tiles per trip so both LDS buffers are static ----
+  issue_tile(0, lds_k0, lds_v0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    if (kt + 1 < nkt) issue_tile(kt + 1, lds_k1, lds_v1);
+    if (wave_active) compute_tile(kt, lds_k0, lds_v0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (kt + 1 >= nkt) break;
+    if (kt + 2 < nkt) issue_tile(kt + 2, lds_k0, lds_v0);
+    if (wave_active) compute_tile(kt + 1, lds_k1, lds_v1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+
+  // ---- epilogue: O / l in bf16, LSE = r + ln l, skipped-tile count ----
+  long long T = 0, qb_total = 0, qb_off = 0;
+  if (p.cu_seqlens != nullptr) {
+    T = p.cu_seqlens[p.nseq];
+    for (int i = 0; i < p.nseq; ++i) {
+      const long long n = ((long long)p.cu_seqlens[i + 1] - p.cu_seqlens[i] + kBQ - 1) / kBQ;
+      if (i < b) qb_off += n;
+      qb_total += n;
+    }
+  }
+  uint16_t* __restrict__ op = p.o + base;
+  const long long ts = p.tok_stride;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const float lt = halves_sum(l[qs]);
+    const float inv = 1.f / lt;
+    const int row = wrow0 + 32 * qs + c;
+    if (row < S_b) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 w;
+          w.x = pack_bf16(oacc[db][qs][4 * g] * inv, oacc[db][qs][4 * g + 1] * inv);
+          w.y = pack_bf16(oacc[db][qs][4 * g + 2] * inv, oacc[db][qs][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(op + (long long)row * ts + 32 * db + 8 * g + 4 * hf) = w;
+        }
+      if (p.lse != nullptr && hf == 0) {
+        const float lse = mb_ref[qs] * (1.f / kLog2e) + logf(lt);
+        if (p.cu_seqlens != nullptr)
+          p.lse[(long long)h * T + tok0 + row] = lse;
+        else
+          p.lse[((long long)b * p.H + h) * p.S + row] = lse;
+      }
+    }
+  }
+  if (p.counts != nullptr && lane == 0) {
+    if (p.cu_seqlens != nullptr) {
+      p.counts[(long long)h * qb_total + qb_off + qb] = nskip;
+    } else {
+      const long long nqb = (p.S + kBQ - 1) / kBQ;
+      p.counts[((long long)b * p.H + h) * nqb + qb] = nskip;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(SSA_ERR_DEVICE, "no HIP device is available");
+  }
+  if (dev < kMaxDevices) {
+    const int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (known == 1) return SSA_OK;
+    if (known == -1) return fail(SSA_ERR_DEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SSA_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+  if (!ok) return fail(SSA_ERR_DEVICE, "device %d is %s, this library runs on gfx950 only", dev, prop.gcnArchName);
+  return SSA_OK;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+int check_tensors(const void* q, const void* k, const void* v, const void* o, const float* lse, int H, int D, float scale) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(SSA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(SSA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (D != kD) return fail(SSA_ERR_UNSUPPORTED, "head dimension %d is not supported (only 128)", D);
+  if (H < 0) return fail(SSA_ERR_INVALID_ARG, "negative head count");
+  if (H > 65535) return fail(SSA_ERR_UNSUPPORTED, "more than 65535 heads");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SSA_ERR_INVALID_ARG, "scale must be finite and positive");
+  return SSA_OK;
+}
+
+// ln(lambda) for one sequence; lambda computed in double, its log rounded to float.
+int resolve(int mode, double p0, double p1, double p2, int seqlen, float* ln_lambda, int* vote) {
+  double lam = 0.0;
+  switch (mode) {
+    case SSA_MODE_FACTOR:
+      if (!std::isfinite(p0) || p0 < 0.0) return fail(SSA_ERR_BAD_THRESHOLD, "factor must be finite and >= 0");
+      if (seqlen <= 0) return fail(SSA_ERR_BAD_THRESHOLD, "seqlen must be > 0");
+      lam = p0 / (double)seqlen;
+      break;
+    case SSA_MODE_THRESHOLD:
+      if (!std::isfinite(p0) || p0 < 0.0) return fail(SSA_ERR_BAD_THRESHOLD, "threshold must be finite and >= 0");
+      lam = p0;
+      break;
+    case SSA_MODE_CALIBRATED: {
+      if (!std::isfinite(p0) || !std::isfinite(p1) || !(p0 > 0.0))
+        return fail(SSA_ERR_NO_CALIBRATION,
+                    "calibrated threshold needs finite coefficients with a > 0; "
+                    "without a calibration use the threshold entry (ssa_fwd_threshold)");
+      if (!std::isfinite(p2)) return fail(SSA_ERR_BAD_THRESHOLD, "target_sparsity must be finite");
+      if (seqlen <= 0) return fail(SSA_ERR_BAD_THRESHOLD, "seqlen must be > 0");
+      lam = p0 * std::exp(p1 * p2) / (double)seqlen;
+      break;
+    }
+    default:
+      return fail(SSA_ERR_INVALID_ARG, "unknown threshold mode %d", mode);
+  }
+  if (!std::isfinite(lam) || lam < 0.0) return fail(SSA_ERR_BAD_THRESHOLD, "lambda is not finite");
+  *vote = lam > 0.0 ? 1 : 0;
+  *ln_lambda = lam > 0.0 ? (float)std::log(lam) : 0.f;
+  return SSA_OK;
+}
+
+template <bool kDebug>
+int launch(const Params& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL(ssa_fwd_kernel<kDebug>, grid, dim3(kThreads), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SSA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return SSA_OK;
+}
+
+int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
+              float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* counts, uint8_t* mask,
+              float* margin, void* stream, bool debug) {
+  int st = check_tensors(q, k, v, o, lse, H, D, scale);
+  if (st != SSA_OK) return st;
+  if (B < 0 || S < 0) return fail(SSA_ERR_INVALID_ARG, "negative batch or sequence length");
+  if (B > 65535) return fail(SSA_ERR_UNSUPPORTED, "batch above 65535");
+  // Per-(batch, head) byte offsets, padded to whole tiles, must fit 32 bits.
+  if (((long long)S + kBK) * kRowBytes + kRowBytes >= (1LL << 32))
+    return fail(SSA_ERR_UNSUPPORTED, "sequence length %d too large", S);
+  if (counts != nullptr && !aligned(counts, 4)) return fail(SSA_ERR_INVALID_ARG, "skip_counts must be 4-byte aligned");
+  if (margin != nullptr && !aligned(margin, 4)) return fail(SSA_ERR_INVALID_ARG, "tile_margin must be 4-byte aligned");
+  if (debug && mask == nullptr) return fail(SSA_ERR_INVALID_ARG, "tile_mask must not be NULL");
+  Params p{};
+  st = resolve(mode, p0, p1, p2, seqlen, &p.ln_lambda, &p.vote);
+  if (st != SSA_OK) return st;
+  if (B == 0 || H == 0 || S == 0) return SSA_OK;
+  st = check_device();
+  if (st != SSA_OK) return st;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.counts = counts;
+  p.mask = mask;
+  p.margin = margin;
+  p.cu_seqlens = nullptr;
+  p.nseq = B;
+  p.H = H;
+  p.S = S;
+  p.qgroups = (S + kRowsPerWG - 1) / kRowsPerWG;
+  p.tok_stride = kD;
+  p.head_stride = (long long)S * kD;
+  p.seq_stride = (long long)H * S * kD;
+  p.scale = scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.lambda_per_seq = 0;
+  const dim3 grid(p.qgroups, H, B);
+  return debug ? launch<true>(p, grid, static_cast<hipStream_t>(stream))
+               : launch<false>(p, grid, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
+            float scale, float factor, int seqlen, int32_t* skip_counts, void* stream) {
+  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, SSA_MODE_FACTOR, factor, 0.0, 0.0, seqlen, skip_counts,
+                   nullptr, nullptr, stream, false);
+}
+
+int ssa_fwd_threshold(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
+                      float scale, float threshold, int32_t* skip_counts, void* stream) {
+  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, SSA_MODE_THRESHOLD, threshold, 0.0, 0.0, S, skip_counts,
+                   nullptr, nullptr, stream, false);
+}
+
+int ssa_fwd_calibrated(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
+                       int D, float scale, float a, float b, float target_sparsity, int seqlen, int32_t* skip_counts,
+                       void* stream) {
+  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, SSA_MODE_CALIBRATED, a, b, target_sparsity, seqlen,
+                   skip_counts, nullptr, nullptr, stream, false);
+}
+
+int ssa_fwd_debug(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
+                  float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* skip_counts,
+                  uint8_t* tile_mask, float* tile_margin, void* stream) {
+  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, tile_mask,
+                   tile_margin, stream, true);
+}
+
+int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+                   int nseq, int max_seqlen, int H, int D, float scale, int mode, double p0, double p1, double p2,
+                   int32_t* skip_counts, void* stream) {
+  int st = check_tensors(q, k, v, o, lse, H, D, scale);
+  if (st != SSA_OK) return st;
+  if (cu_seqlens == nullptr || !aligned(cu_seqlens, 4)) return fail(SSA_ERR_INVALID_ARG, "cu_seqlens must be a 4-byte aligned device pointer");
+  if (nseq < 0 || max_seqlen < 0) return fail(SSA_ERR_INVALID_ARG, "negative nseq or max_seqlen");
+  if (nseq > 65535) return fail(SSA_ERR_UNSUPPORTED, "more than 65535 sequences");
+  if (((long long)max_seqlen + kBK) * H * kRowBytes + kRowBytes >= (1LL << 32))
+    return fail(SSA_ERR_UNSUPPORTED, "max_seqlen x heads too large for 32-bit offsets");
+  if (skip_counts != nullptr && !aligned(skip_counts, 4)) return fail(SSA_ERR_INVALID_ARG, "skip_counts must be 4-byte aligned");
+  Params p{};
+  // Validate the control once with a representative length; the kernel
+  // recomputes ln(lambda_b) for each sequence's own length.
+  st = resolve(mode, p0, p1, p2, max_seqlen > 0 ? max_seqlen : 1, &p.ln_lambda, &p.vote);
+  if (st != SSA_OK) return st;
+  if (nseq == 0 || H == 0 || max_seqlen == 0) return SSA_OK;
+  st = check_device();
+  if (st != SSA_OK) return st;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.counts = skip_counts;
+  p.cu_seqlens = cu_seqlens;
+  p.nseq = nseq;
+  p.H = H;
+  p.S = max_seqlen;
+  p.qgroups = (max_seqlen + kRowsPerWG - 1) / kRowsPerWG;
+  p.tok_stride = (long long)H * kD;
+  p.head_stride = kD;
+  p.seq_stride = 0;
+  p.scale = scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  if (mode == SSA_MODE_THRESHOLD) {
+    p.lambda_per_seq = 0;
+  } else {
+    p.lambda_per_seq = 1;
+    p.factor = mode == SSA_MODE_FACTOR ? p0 : p0 * std::exp(p1 * p2);
+  }
+  const dim3 grid(p.qgroups, H, nseq);
+  return launch<false>(p, grid, static_cast<hipStream_t>(stream));
+}
+
+int ssa_resolve_threshold(int mode, double p0, double p1, double p2, int seqlen, float* ln_lambda,
+                          int* vote_enabled) {
+  if (ln_lambda == nullptr || vote_enabled == nullptr) return fail(SSA_ERR_INVALID_ARG, "NULL output pointer");
+  return resolve(mode, p0, p1, p2, seqlen, ln_lambda, vote_enabled);
+}
+
+int ssa_device_check(void) { return check_device(); }
+
+const char* ssa_strerror(int status) {
+  switch (status) {
+    case SSA_OK: return "SSA_OK";
+    case SSA_ERR_INVALID_ARG: return "SSA_ERR_INVALID_ARG: invalid argument";
+    case SSA_ERR_UNSUPPORTED: return "SSA_ERR_UNSUPPORTED: unsupported shape";
+    case SSA_ERR_BAD_THRESHOLD: return "SSA_ERR_BAD_THRESHOLD: threshold, factor or seqlen out of range";
+    case SSA_ERR_NO_CALIBRATION: return "SSA_ERR_NO_CALIBRATION: missing calibration, use the threshold entry";
+    case SSA_ERR_DEVICE: return "SSA_ERR_DEVICE: no gfx950 device";
+    case SSA_ERR_LAUNCH: return "SSA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown ssa_status";
+  }
+}
+
+const char* ssa_last_error(void) { return g_last_error; }
+
+int ssa_version(void) { return 1; }
+
+}  // extern "C"

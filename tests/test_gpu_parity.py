@@ -1,0 +1,230 @@
+"""HIP library against the CPU oracle on seeded inputs (parity proper).
+
+Sizes here let the oracle finish in seconds while still spanning several
+64 x 128 tiles and ragged tails; the full-size workloads are in
+test_gpu_full.py.  Each case runs the product entry point twice
+(determinism), the debug entry point (tile mask), and compares with the
+oracle as tests/parity.py describes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from skip_softmax_flashattention_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssa():
+    import skip_softmax_flashattention_amd as m
+    m.device_check()
+    return m
+
+
+def _run(ssa, w, name, **kw):
+    print(f"[case] {name} shape={tuple(w.q.shape)} {kw}", flush=True)
+    rep = parity.check_fixed(ssa, w, **kw)
+    print(f"[case] {name}: {rep}", flush=True)
+    parity.assert_bar(rep)
+    return rep
+
+
+# ---- Tiny workload: B=1, H=2, S=1024; factor in {0, 0.5, 4.0} ----------------
+@pytest.mark.parametrize("factor", [0.0, 0.5, 4.0])
+def test_tiny(ssa, factor):
+    w = inputs.tiny()
+    rep = _run(ssa, w, "tiny", factor=factor)
+    if factor == 0.0:
+        assert rep.skipped == 0
+
+
+def test_tiny_dense_matches_dense_oracle(ssa):
+    """lambda = 0 is dense attention: compare with the float64 dense oracle too."""
+    w = inputs.tiny()
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    o, lse, cnt = ssa.fwd(q, k, v, factor=0.0)
+    torch.cuda.synchronize()
+    od, lsed = oracle.dense_attention(*(oracle.from_bf16(t) for t in (w.q, w.k, w.v)), w.scale)
+    err = np.abs(o.float().cpu().numpy() - od)
+    assert err.max() <= parity.O_MAX and err.mean() <= parity.O_MEAN
+    assert np.abs(lse.cpu().numpy() - lsed).max() <= parity.LSE_MAX
+    assert int(cnt.sum()) == 0
+
+
+# ---- planted dominant key: every tile after the first is skipped -----------------
+def _planted(seed=22, S=640, B=1, H=2):
+    rng = np.random.default_rng(seed)
+    D = 128
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = 0.2 * rng.standard_normal((B, H, S, D)) + 3.0 * u
+    k = 0.2 * rng.standard_normal((B, H, S, D))
+    k[:, :, 5] = 40.0 * u
+    v = rng.standard_normal((B, H, S, D))
+    t = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    return inputs.Workload("planted", t(q), t(k), t(v))
+
+
+def test_planted_all_later_tiles_skipped(ssa):
+    w = _planted()
+    rep = _run(ssa, w, "planted", threshold=1e-3)
+    nqb, nkt = 10, 5
+    assert rep.skipped == 2 * nqb * (nkt - 1)
+    # the output is softmax attention over tile 0 alone
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    o, _, _ = ssa.fwd(q, k, v, threshold=1e-3)
+    qd, kd, vd = (oracle.from_bf16(t[0, 0]) for t in (w.q, w.k, w.v))
+    ref, _ = oracle.dense_head(qd, kd[:128], vd[:128], w.scale)
+    assert np.abs(o[0, 0].float().cpu().numpy() - ref).max() <= parity.O_MAX
+
+
+# ---- grid-local inputs with ragged tails and mixed decisions ----------------------
+@pytest.mark.parametrize("grid", [(3, 10, 13), (4, 16, 17), (2, 32, 33)])
+@pytest.mark.parametrize("lam", [1e-6, 1e-3, 0.05, 0.5])
+def test_grid_ragged(ssa, grid, lam):
+    w = inputs.grid_small(5, grid, heads=2)
+    _run(ssa, w, f"grid{grid}", threshold=lam)
+
+
+def test_grid_mixed_decisions_exist(ssa):
+    """The grid workload really exercises both branches of the vote."""
+    w = inputs.grid_small(5, (4, 16, 17), heads=2)
+    rep = _run(ssa, w, "grid-mixed", threshold=0.5)
+    assert 0.1 < rep.skipped / rep.tiles < 0.9
+
+
+# ---- edge sizes --------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 511, 513])
+def test_edge_lengths(ssa, S):
+    w = inputs.random_qkv(100 + S, 2, 3, S, qk_gain=2.0)
+    _run(ssa, w, f"edge S={S}", factor=0.3 * S)
+
+
+def test_many_heads_small(ssa):
+    w = inputs.random_qkv(7, 3, 17, 200, qk_gain=2.0)
+    _run(ssa, w, "B3H17", factor=0.0)
+
+
+def test_seqlen_argument_normalises(ssa):
+    """factor / seqlen with seqlen != S (the caller's max_kv_len)."""
+    w = inputs.grid_small(9, (3, 10, 13), heads=2)
+    _run(ssa, w, "seqlen", factor=20.0, seqlen=100)
+
+
+# ---- the three controls --------------------------------------------------------------
+def test_threshold_entry_equals_factor_entry(ssa):
+    w = inputs.grid_small(11, (4, 16, 17), heads=2)
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    S = q.shape[2]
+    a = ssa.fwd(q, k, v, threshold=0.02)
+    b = ssa.fwd(q, k, v, factor=0.02 * S)
+    torch.cuda.synchronize()
+    # equal lambda up to rounding of 0.02 * S / S: same decisions here
+    assert torch.equal(a[2], b[2])
+
+
+def test_calibrated_entry(ssa):
+    w = inputs.grid_small(12, (4, 16, 17), heads=2)
+    _run(ssa, w, "calibrated", calib=(3.0, 4.4, 0.5))
+
+
+def test_lambda_above_one(ssa):
+    """Thresholds above 1 are accepted; later decisions depend on earlier ones."""
+    w = inputs.grid_small(13, (3, 10, 13), heads=2)
+    _run(ssa, w, "lambda>1", threshold=3.0)
+
+
+# ---- Mid workload: B=2, H=8, S=4096, k = q ----------------------------------------------
+@pytest.mark.parametrize("lam", [1e-4, 1e-3, 1e-2])
+def test_mid(ssa, lam):
+    w = inputs.mid()
+    _run(ssa, w, "mid", threshold=lam)
+
+
+# ---- packed variable-length batches ---------------------------------------------------
+def _varlen_check(ssa, w, mode_kw, lambdas):
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    cu = w.cu_seqlens.cuda()
+    o, lse, cnt = ssa.fwd_varlen(q, k, v, cu, max(w.seqlens), scale=w.scale, **mode_kw)
+    o2, lse2, cnt2 = ssa.fwd_varlen(q, k, v, cu, max(w.seqlens), scale=w.scale, **mode_kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(cnt, cnt2)
+    o_np, lse_np, cnt_np = o.float().cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
+    qd, kd, vd = (oracle.from_bf16(t) for t in (w.q, w.k, w.v))
+    cuh = w.cu_seqlens.tolist()
+    reports, off = [], 0
+    for bi, n in enumerate(w.seqlens):
+        r0, r1 = cuh[bi], cuh[bi + 1]
+        ln = oracle.ln_lambda_f32(lambdas[bi])
+        nqb = -(-n // 64)
+        for h in range(q.shape[1]):
+            # The product entry reports counts, not the mask: compare counts with
+            # the oracle's own decisions and the output with the oracle forced to
+            # those decisions (no tile of these inputs sits inside the band).
+            own = oracle.skip_head(qd[r0:r1, h], kd[r0:r1, h], vd[r0:r1, h], w.scale, ln)
+            if ln is not None:
+                band = np.abs(own.margin.astype(np.float64) - float(ln)) <= parity.MASK_BAND
+                assert not band.any(), "a tile sits inside the threshold band; pick another lambda"
+            assert (cnt_np[h, off:off + nqb] == own.skipped.sum(1)).all()
+            err = np.abs(o_np[r0:r1, h] - own.o.reshape(-1, 128)[:n])
+            lerr = np.abs(lse_np[h, r0:r1] - own.lse.reshape(-1)[:n])
+            reports.append(parity.Report(own.skipped.size, int(own.skipped.sum()), 0, float(err.max()),
+                                         float(err.mean()), float(lerr.max())))
+        off += nqb
+    rep = parity.merge(reports)
+    print(f"[case] varlen {w.seqlens} {mode_kw}: {rep}", flush=True)
+    parity.assert_bar(rep)
+    return rep
+
+
+VARLEN_SMALL = ((1, 7, 10), (3, 10, 13), (2, 8, 9), (1, 1, 1))
+
+
+@pytest.mark.parametrize("factor", [0.0, 0.02, 3.0])
+def test_varlen_factor(ssa, factor):
+    w = inputs.varlen(seed=21, heads=3, grids=VARLEN_SMALL)
+    lams = [oracle.resolve_lambda(factor=factor, seqlen=n) for n in w.seqlens]
+    rep = _varlen_check(ssa, w, dict(factor=factor), lams)
+    if factor == 0.0:
+        assert rep.skipped == 0
+
+
+def test_varlen_threshold_and_calibrated(ssa):
+    w = inputs.varlen(seed=22, heads=2, grids=VARLEN_SMALL)
+    lams = [oracle.resolve_lambda(threshold=0.01)] * len(w.seqlens)
+    _varlen_check(ssa, w, dict(threshold=0.01), lams)
+    a, b, s = 0.5, 4.0, 0.6
+    lams = [oracle.resolve_lambda(a=a, b=b, target_sparsity=s, seqlen=n) for n in w.seqlens]
+    _varlen_check(ssa, w, dict(calib=(a, b, s)), lams)
+
+
+def test_varlen_with_empty_sequence(ssa):
+    w = inputs.varlen(seed=23, heads=2, grids=((2, 5, 7), (3, 10, 13)))
+    # insert an empty sequence in the middle
+    cu = w.cu_seqlens.tolist()
+    w.cu_seqlens = torch.tensor([cu[0], cu[1], cu[1], cu[2]], dtype=torch.int32)
+    w.seqlens = [w.seqlens[0], 0, w.seqlens[1]]
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    o, lse, cnt = ssa.fwd_varlen(q, k, v, w.cu_seqlens.cuda(), max(w.seqlens), factor=0.0)
+    torch.cuda.synchronize()
+    od, lsed, _, _ = oracle.skip_attention_varlen(*(oracle.from_bf16(t) for t in (w.q, w.k, w.v)),
+                                                   w.cu_seqlens.tolist(), w.scale, [0.0, 0.0, 0.0])
+    assert np.abs(o.float().cpu().numpy() - od).max() <= parity.O_MAX
+    assert np.abs(lse.cpu().numpy() - lsed).max() <= parity.LSE_MAX
+
+
+def test_errors_on_gpu(ssa):
+    w = inputs.random_qkv(1, 1, 1, 64)
+    q = w.q.cuda()
+    with pytest.raises(ssa.SsaError) as e:
+        ssa.fwd(q, q, q, factor=-1.0)
+    assert e.value.code == -3
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ssa.SsaError) as e:
+        ssa.fwd(x, x, x, factor=1.0)
+    assert e.value.code == -2
