@@ -1,0 +1,222 @@
+"""Benchmark of the Skip-Softmax FlashAttention forward on one MI355X.
+
+Workload: Wan-like video self-attention, B=1, H=40, S=32760, D=128 (latent
+grid 21 x 30 x 52, seed 2), bf16, inputs resident in HBM.  One step is one
+forward call at the threshold that skips about 75% of the 64 x 128 tiles
+(lambda chosen by the CPU oracle, tests/golden/wan_lambdas.json); every step
+is paired with a dense (lambda = 0) call of the same kernel, interleaved, so
+the speedup is an in-session ratio.
+
+Printed (one JSON line): effective TFLOP/s of the skip step (dense-equivalent
+4 B H S^2 D per call over the call's time) as ``value``; executed TFLOP/s and
+MFMA utilisation against the bf16 dense peak; the dense call's numbers; the
+speedup; a roofline entry for the kernel; and the CPU oracle timed on a
+bounded sample as a baseline only.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak (published)
+METRIC = "effective TFLOP/s + MFMA util at S=32760 H=40 D=128, and speedup vs λ=0 at ~75% skip"
+KERNEL_SRC = os.path.join(ROOT, "skip_softmax_flashattention_amd", "csrc", "ssa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wan_like.json")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def executed_flops(mask, S, D=128, bq=64, bk=128):
+    """2 D r c for QK^T of every tile plus 2 D r c for P.V of every kept tile;
+    r, c the tile's valid rows and keys.  mask: [B, H, nQB, nKT] bool (True = skipped)."""
+    import numpy as np
+    nqb, nkt = mask.shape[-2:]
+    r = np.minimum(bq, S - bq * np.arange(nqb)).astype(np.float64)
+    c = np.minimum(bk, S - bk * np.arange(nkt)).astype(np.float64)
+    rc = r[:, None] * c[None, :]
+    qk = 2.0 * D * rc.sum() * mask.shape[0] * mask.shape[1]
+    pv = 2.0 * D * (rc[None, None] * (~mask)).sum()
+    return qk + pv
+
+
+def issued_mfma_flops(mask, D=128, bq=64, bk=128):
+    """Padded MFMA work issued: every tile runs a full 64 x 128 QK^T, kept tiles a full P.V."""
+    tiles = mask.size
+    kept = int((~mask).sum())
+    return 2.0 * D * bq * bk * (tiles + kept)
+
+
+def cpu_baseline(w, ln_lambda, seconds):
+    """The oracle's recurrence on q-blocks of head 0, sized to about ``seconds``."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    qd, kd, vd = (oracle.from_bf16(t[0, 0]) for t in (w.q, w.k, w.v))
+    S = qd.shape[0]
+    rng = np.random.default_rng(7)
+
+    def run(n):
+        qbs = np.sort(rng.choice(-(-S // 64), n, replace=False))
+        t0 = time.perf_counter()
+        r = oracle.skip_head(qd, kd, vd, w.scale, ln_lambda, qblocks=qbs)
+        dt = time.perf_counter() - t0
+        rows = np.minimum(64, S - 64 * qbs).astype(np.float64)
+        c = np.minimum(128, S - 128 * np.arange(r.skipped.shape[1])).astype(np.float64)
+        fl = 2.0 * 128 * (rows[:, None] * c[None, :] * (1 + (~r.skipped))).sum()
+        return dt, fl
+
+    dt, fl = run(2)
+    n = int(min(512, max(2, round(2 * seconds / max(dt, 1e-3)))))
+    dt, fl = run(n)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of 512 query blocks (64 rows x all 256 key tiles) of head 0 at the same lambda; "
+                      f"float64 numpy recurrence, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--target", type=float, default=0.75, help="skip fraction of the timed step")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "multi-GPU sharding of this kernel is not built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import skip_softmax_flashattention_amd as ssa
+    from skip_softmax_flashattention_amd import inputs
+
+    ssa.device_check()
+    dev = torch.device("cuda:0")
+    with open(os.path.join(ROOT, "tests", "golden", "wan_lambdas.json")) as f:
+        lam = json.load(f)["lambda"][str(args.target)]
+    w = inputs.wan()
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    B, H, S, D = q.shape
+    factor = lam * S
+    dense_flops = 4.0 * B * H * S * S * D
+
+    # Tile decisions of the timed configuration (debug entry point, outside the timed region).
+    _, _, cnt_dbg, mask, _ = ssa.fwd_debug(q, k, v, factor=factor, scale=w.scale)
+    torch.cuda.synchronize()
+    mask_np = mask.cpu().numpy().astype(bool)
+    skip_frac = float(mask_np.mean())
+    exec_flops = executed_flops(mask_np, S)
+    mfma_flops = issued_mfma_flops(mask_np)
+    del mask
+
+    def dense():
+        return ssa.fwd(q, k, v, factor=0.0, scale=w.scale)
+
+    def skip():
+        return ssa.fwd(q, k, v, factor=factor, scale=w.scale)
+
+    for _ in range(args.warmup):
+        dense()
+        skip()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        dense()
+        ev[i][1].record(stream)
+        ev[i][2].record(stream)
+        _, _, cnt = skip()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_dense = np.array([a[0].elapsed_time(a[1]) for a in ev])
+    ms_skip = np.array([a[2].elapsed_time(a[3]) for a in ev])
+    assert int(cnt.sum()) == int(cnt_dbg.sum()) == int(mask_np.sum()), "skip counts changed between calls"
+
+    t_d, t_s = float(ms_dense.mean()), float(ms_skip.mean())
+    eff = dense_flops / (t_s * 1e-3) / 1e12
+    exe = exec_flops / (t_s * 1e-3) / 1e12
+    dense_tf = dense_flops / (t_d * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha256_16") == kernel_hash():
+            traffic = tr.get("traffic")
+
+    out = {
+        "metric": METRIC,
+        "value": round(eff, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_s, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded grid-local positional embedding + noise (no model activations)",
+        "config": {
+            "workload": "wan-like video DiT self-attention, B=1 H=40 S=32760 D=128, grid 21x30x52, seed 2",
+            "lambda": lam, "factor": factor, "target_skip_fraction": args.target,
+            "achieved_skip_fraction": round(skip_frac, 4), "tile": "64x128", "causal": False,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(exe, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(exe / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "skip_step": {
+            "ms_mean": round(t_s, 4), "ms_min": round(float(ms_skip.min()), 4),
+            "ms_median": round(float(np.median(ms_skip)), 4),
+            "effective_tflops": round(eff, 2), "executed_tflops": round(exe, 2),
+            "mfma_util_issued": round(mfma_flops / (t_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "executed_tflop_per_call": round(exec_flops / 1e12, 4),
+        },
+        "dense_step": {
+            "ms_mean": round(t_d, 4), "ms_min": round(float(ms_dense.min()), 4),
+            "ms_median": round(float(np.median(ms_dense)), 4),
+            "tflops": round(dense_tf, 2), "mfma_util": round(dense_tf / PEAK_BF16_TFLOPS, 4),
+            "tflop_per_call": round(dense_flops / 1e12, 4),
+        },
+        "speedup_vs_dense": round(t_d / t_s, 4),
+        "timed_wall_s": round(t_wall, 3),
+        "kernel_sha256_16": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = cpu_baseline(w, oracle.ln_lambda_f32(oracle.resolve_lambda(factor=factor, seqlen=S)),
+                                           args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

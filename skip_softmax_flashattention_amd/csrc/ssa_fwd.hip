@@ -118,6 +118,18 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The vote's arithmetic, rounded step by step (never fused into an FMA):
+// tile_max = fl(raw_max * scale), margin = fl(tile_max - m).  Every entry
+// point then takes bit-identical decisions.
+__device__ __forceinline__ float scaled_max(float raw_max, float scale) {
+#pragma clang fp contract(off)
+  return raw_max * scale;
+}
+__device__ __forceinline__ float vote_margin(float tile_max, float m) {
+#pragma clang fp contract(off)
+  return tile_max - m;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
@@ -272,10 +284,10 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_fwd_kernel(const Params p) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qs][r]);
-      tmax[qs] = halves_max(mx) * p.scale;
+      tmax[qs] = scaled_max(halves_max(mx), p.scale);
     }
-    const float d0 = tmax[0] - m_run[0];
-    const float d1 = tmax[1] - m_run[1];
+    const float d0 = vote_margin(tmax[0], m_run[0]);
+    const float d1 = vote_margin(tmax[1], m_run[1]);
     const bool pass = (!valid0 || d0 < ln_lambda) && (!valid1 || d1 < ln_lambda);
     const bool skip = vote && (__builtin_amdgcn_ballot_w64(!pass) == 0);
 

@@ -1,0 +1,104 @@
+"""Full-size workloads in the launch configuration the benchmark times.
+
+The oracle cannot do the whole 22 TFLOP problem on the CPU, so each case
+checks every output that is cheap to check and samples the rest:
+  * determinism and product/debug agreement over the whole problem;
+  * skip_counts equal to the debug mask's row sums everywhere;
+  * tile mask, O and LSE against the oracle on seeded samples of query blocks
+    (rows are independent given K and V, so a sampled block is exact);
+  * lambda = 0 skips nothing.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from skip_softmax_flashattention_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def ssa():
+    import skip_softmax_flashattention_amd as m
+    m.device_check()
+    return m
+
+
+@pytest.fixture(scope="module")
+def wan():
+    return inputs.wan()
+
+
+def _whole_problem_checks(ssa, q, k, v, scale, **kw):
+    o1, l1, c1 = ssa.fwd(q, k, v, scale=scale, **kw)
+    o2, l2, c2 = ssa.fwd(q, k, v, scale=scale, **kw)
+    od, ld, cd, mask, margin = ssa.fwd_debug(q, k, v, scale=scale, **kw)
+    torch.cuda.synchronize()
+    msum = mask.sum(-1, dtype=torch.int32)
+    print(f"[full] counts: fwd#1 {int(c1.sum())} fwd#2 {int(c2.sum())} debug {int(cd.sum())} "
+          f"mask {int(mask.sum())}; O equal 1-2 {torch.equal(o1, o2)} 1-debug {torch.equal(o1, od)}", flush=True)
+    assert torch.equal(cd, msum), "debug counts differ from the debug mask"
+    assert torch.equal(c1, c2) and torch.equal(o1, o2) and torch.equal(l1, l2), "product entry not deterministic"
+    assert torch.equal(c1, cd), "product and debug entry points disagree on skip counts"
+    assert torch.equal(o1, od) and torch.equal(l1, ld), "product and debug entry points disagree on O / LSE"
+    assert torch.isfinite(l1).all()
+    return o1, l1, c1, mask.cpu().numpy().astype(bool)
+
+
+def _sampled(w, ln, o, lse, cnt, mask, heads, per_head, seed):
+    rng = np.random.default_rng(seed)
+    B, H, S, D = w.q.shape
+    nqb = -(-S // 64)
+    o_np, lse_np, cnt_np = o.float().cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
+    reports = []
+    for h in heads:
+        qbs = np.sort(rng.choice(nqb, per_head, replace=False))
+        if nqb - 1 not in qbs:
+            qbs[-1] = nqb - 1          # always include the ragged last block
+        rows = (qbs[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+        rows = rows[rows < S]
+        qd, kd, vd = (oracle.from_bf16(t[0, h]) for t in (w.q, w.k, w.v))
+        reports.append(parity.compare_head_blocks(qd, kd, vd, w.scale, ln, qbs, mask[0, h][qbs], o_np[0, h][rows],
+                                                  lse_np[0, h][rows], cnt_np[0, h][qbs]))
+    return parity.merge(reports)
+
+
+def _lam(frac):
+    with open(os.path.join(GOLDEN, "wan_lambdas.json")) as f:
+        return json.load(f)["lambda"][frac]
+
+
+@pytest.mark.parametrize("frac", ["0", "0.5", "0.75", "0.9"])
+def test_wan_like(ssa, wan, frac):
+    S = wan.q.shape[2]
+    lam = 0.0 if frac == "0" else _lam(frac)
+    print(f"[case] wan-like S={S} H=40 target skip {frac} lambda {lam:.6g}", flush=True)
+    q, k, v = (t.cuda() for t in (wan.q, wan.k, wan.v))
+    o, lse, cnt, mask = _whole_problem_checks(ssa, q, k, v, wan.scale, factor=lam * S)
+    ln = oracle.ln_lambda_f32(oracle.resolve_lambda(factor=lam * S, seqlen=S))
+    rep = _sampled(wan, ln, o, lse, cnt, mask, heads=(0, 17, 39), per_head=6, seed=int(float(frac) * 100))
+    print(f"[case] wan-like {frac}: whole-problem skip fraction {mask.mean():.4f}; sampled {rep}", flush=True)
+    parity.assert_bar(rep)
+    if frac == "0":
+        assert not mask.any()
+    else:
+        assert abs(mask.mean() - float(frac)) < 0.05
+
+
+def test_long_sequence(ssa):
+    w = inputs.long_seq()
+    S = w.q.shape[2]
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    for lam in (0.0, 1e-3):
+        print(f"[case] long S={S} H=24 threshold {lam}", flush=True)
+        o, lse, cnt, mask = _whole_problem_checks(ssa, q, k, v, w.scale, threshold=lam)
+        ln = oracle.ln_lambda_f32(lam)
+        rep = _sampled(w, ln, o, lse, cnt, mask, heads=(0, 23), per_head=6, seed=3)
+        print(f"[case] long {lam}: whole-problem skip fraction {mask.mean():.4f}; sampled {rep}", flush=True)
+        parity.assert_bar(rep)
