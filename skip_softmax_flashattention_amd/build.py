@@ -33,8 +33,6 @@ def command() -> list:
         "-I" + INCLUDE,
         # no packed fp32 instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA results in VGPRs: the score tile is post-processed by VALU code
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-o", OUT + ".tmp", SRC,
     ]
 

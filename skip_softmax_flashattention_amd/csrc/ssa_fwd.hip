@@ -5,35 +5,42 @@
 // "The online-softmax pass" and "The skip test".  The C ABI is declared in
 // include/ssa.h.
 //
-// Work decomposition.  One workgroup = 4 waves = 256 query rows of one
-// (sequence, head).  Each wave owns one 64-row query block, which is exactly
-// one vote group of the skip test, so the all-rows vote is a single wave
-// ballot with no cross-wave traffic.  Key tiles of 128 keys stream through
-// LDS, double buffered, shared by the four waves.  Tiles are copied from
-// global memory straight into LDS (buffer loads with the LDS-destination
-// bit), so staging costs no registers; keys past the end of the sequence lie
-// outside the buffer resource's range and arrive as zeros.
+// Work decomposition.  One workgroup = 8 waves = 256 query rows of one
+// (sequence, head); each wave owns 32 rows, and the two waves 2g, 2g+1 form
+// the 64-row vote group g of the skip test.  Key tiles of 128 keys stream
+// through LDS (K and V double buffered, shared by all eight waves), copied
+// from global memory straight into LDS by buffer loads with the
+// LDS-destination bit; keys past the end of the sequence lie outside the
+// buffer resource's range and arrive as zeros.
 //
-// MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  A wave
-// computes the transposed score tile S^T = K Q^T as 4 key sub-blocks x 2
-// query sub-blocks of 32 x 32.  In the 32x32 accumulator layout a lane holds
-// one query column and 16 key rows, so each lane owns two query rows (c and
-// 32 + c) and 64 of the tile's 128 keys: the row maximum and row sum are
-// in-lane reductions plus one exchange between the two wave halves.  The key
-// rows of the K operand are permuted so that a lane's accumulator registers
-// 8t..8t+7 hold 8 *consecutive* keys; rounded to bf16 they are directly the
-// B operand (P^T) of O^T = V^T P^T.  The A operand V^T comes from the
-// natural-layout V tile through two LDS transpose reads (ds_read_b64_tr_b16).
+// Ping-pong schedule.  Two waves share each SIMD.  Waves 0-3 (group A) and
+// 4-7 (group B) run the same two-cluster program per tile, B one cluster
+// behind A, with a workgroup barrier between clusters:
+//   C1  scores S^T = K Q^T (MFMA) with the row maximum folded in, then this
+//       wave's half of the vote, published in LDS
+//   C2  the vote group's decision; kept tiles: exponentials (VALU) of each
+//       32-key block interleaved with the P.V MFMAs of the previous block
+// so while one wave of a SIMD runs its QK^T MFMAs the other runs the
+// softmax and P.V of the previous tile, and the two halves of a vote group
+// exchange their votes across the C1/C2 barrier.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  S^T is
+// 4 key blocks of 32 x 32: a lane holds one query row and 16 keys per block,
+// so row reductions are in-lane plus one exchange between the wave halves.
+// The K operand's rows are permuted so that accumulator registers 8t..8t+7
+// hold 8 consecutive keys; rounded to bf16 they are directly the B operand
+// (P^T) of O^T = V^T P^T, whose A operand V^T comes from the natural-layout
+// V tile through LDS transpose reads (ds_read_b64_tr_b16).
 //
 // The skip test runs on fp32 scores in log space before any exponential:
-// tile_max[i] - m[i] < ln(lambda) for every valid row of the wave's block,
+// tile_max[i] - m[i] < ln(lambda) for every valid row of the vote group,
 // m the true running maximum over the kept tiles.  A skipped tile costs only
 // its QK^T and row maximum; m, l and O are left untouched.
 //
 // Exponent reference.  The exponentials use a per-row reference r <= m and
 // O, l are rescaled only when m climbs more than kRescaleLog2 binades above
-// r (then r = m).  This changes only rounding: O / l and r + ln(l) are
-// independent of the reference.  P = exp(s - r) stays below 2^kRescaleLog2.
+// r (then r = m).  This changes only rounding: O / l and r + ln(l) do not
+// depend on the reference, and P = exp(s - r) stays below 2^kRescaleLog2.
 
 #include <hip/hip_runtime.h>
 
@@ -49,15 +56,17 @@
 namespace {
 
 constexpr int kD = 128;
-constexpr int kBQ = 64;                 // query rows per wave = rows per vote group
+constexpr int kBQ = 64;                 // rows per vote group
 constexpr int kBK = 128;                // keys per tile
-constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWG = kBQ * kWaves;
+constexpr int kRowsPerWG = kRowsPerWave * kWaves;
 constexpr int kRowBytes = kD * 2;                  // one bf16 row of 128 channels
 constexpr int kTileBytes = kBK * kRowBytes;        // 32 KB
+constexpr int kCopyPerWave = kTileBytes / (kWaves * 1024);   // 1 KB DMA instructions per wave per tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleLog2 = 10.f;               // P <= 2^10 before a rescale is forced
+constexpr float kRescaleLog2 = 16.f;               // P <= 2^16 before a rescale is forced
 constexpr unsigned kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -100,9 +109,9 @@ __device__ __forceinline__ int swz(int r) {
   return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
 }
 
-// Key row that MFMA row m (0..31) of a 32-key sub-block loads.  With this
+// Key row that MFMA row m (0..31) of a 32-key block loads.  With this
 // permutation accumulator register r of lane half hf holds key
-// 16 * (r / 8) + 8 * hf + (r % 8) of the sub-block.
+// 16 * (r / 8) + 8 * hf + (r % 8) of the block.
 __device__ __forceinline__ int key_perm(int m) {
   const int a = m >> 3, hh = (m >> 2) & 1, j = m & 3;
   return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + j;
@@ -140,15 +149,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 template <bool kDebug>
-__global__ __launch_bounds__(kThreads, 1) void ssa_fwd_kernel(const Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ssa_fwd_kernel(const Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
+  __shared__ int vote_lds[kWaves];
+  __shared__ float margin_lds[kWaves];
 
   const int qg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hf = lane >> 5;
+  const bool group_b = wave >= 4;
 
   long long tok0 = 0;
   int S_b = p.S;
@@ -172,42 +183,37 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_fwd_kernel(const Params p) {
   const bool vote = p.vote != 0;
 
   const int nkt = (S_b + kBK - 1) / kBK;
-  const int qb = qg * kWaves + wave;
-  const int wrow0 = qb * kBQ;
-  const bool wave_active = wrow0 < S_b;
-  const bool valid0 = wrow0 + c < S_b;
-  const bool valid1 = wrow0 + 32 + c < S_b;
+  const int wrow0 = qg * kRowsPerWG + wave * kRowsPerWave;   // this wave's first row
+  const int qb = (qg * kRowsPerWG) / kBQ + (wave >> 1);      // vote group (64-row q-block)
+  const bool valid = wrow0 + c < S_b;
 
-  // Q^T operand fragments: qf[qs][s] = Q[wrow0 + 32 qs + c][16 s + 8 hf .. +7]
-  // (rows past the end read as zeros).
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    const uint32_t off = (uint32_t)(wrow0 + 32 * qs + c) * ts_bytes + 16u * hf;
+  // Q^T operand fragments: qf[s] = Q[wrow0 + c][16 s + 8 hf .. +7] (rows past
+  // the end read as zeros).
+  bf16x8 qf[8];
+  {
+    const uint32_t off = (uint32_t)(wrow0 + c) * ts_bytes + 16u * hf;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      qf[qs][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32u * s, 0, 0));
+      qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 32u * s, 0, 0));
   }
 
   // ---- tile copy: global -> LDS, 16 bytes per lane per instruction ----
-  // Instruction j of wave w fills LDS rows 32 w + 4 j .. +3 (1 KB); lane l
-  // lands at byte 16 l of that block: row 32 w + 4 j + l / 16, physical
-  // chunk l % 16, which holds logical chunk (l % 16) ^ swz(row).
-  uint32_t copy_off[8];
+  // Instruction j of wave w fills LDS rows 4 (kCopyPerWave w + j) .. +3
+  // (1 KB); lane l lands at byte 16 l of that block: row 4 (..) + l / 16,
+  // physical chunk l % 16, which holds logical chunk (l % 16) ^ swz(row).
+  uint32_t copy_off[kCopyPerWave];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 32 * wave + 4 * j + (lane >> 4);
+  for (int j = 0; j < kCopyPerWave; ++j) {
+    const int r = 4 * (kCopyPerWave * wave + j) + (lane >> 4);
     copy_off[j] = (uint32_t)r * ts_bytes + 16u * (uint32_t)((lane & 15) ^ swz(r));
   }
-  auto issue_tile = [&](int kt, unsigned char* kdst, unsigned char* vdst) {
+  auto issue_copy = [&](const __amdgpu_buffer_rsrc_t& rs, int kt, unsigned char* dst) __attribute__((always_inline)) {
     const uint32_t tile_off = (uint32_t)kt * kBK * ts_bytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = (32 * wave + 4 * j) * kRowBytes;
+    for (int j = 0; j < kCopyPerWave; ++j) {
       // The whole offset goes in the per-lane (range-checked) voffset.
-      const uint32_t off = copy_off[j] + tile_off;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(void, kdst + blk), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(void, vdst + blk), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, dst + 4 * (kCopyPerWave * wave + j) * kRowBytes),
+                                               16, copy_off[j] + tile_off, 0, 0, 0);
     }
   };
 
@@ -218,176 +224,203 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_fwd_kernel(const Params p) {
   // V^T operand (A of O^T) via transpose reads: within 16-lane group g the
   // lane 4 e + q supplies row 8 hf + 4 ih + e (plus the 16-key step base),
   // channels 32 db + 16 (g % 2) + 4 q .. +3.
-  const int ve = (lane & 15) >> 2, vq = lane & 3, vg = (lane >> 4) & 1;
   int voff[2][4];
+  {
+    const int ve = (lane & 15) >> 2, vq = lane & 3, vg = (lane >> 4) & 1;
 #pragma unroll
-  for (int ih = 0; ih < 2; ++ih) {
-    const int row = 8 * hf + 4 * ih + ve;
+    for (int ih = 0; ih < 2; ++ih) {
+      const int row = 8 * hf + 4 * ih + ve;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int lc = 4 * db + 2 * vg + (vq >> 1);
-      voff[ih][db] = row * kRowBytes + 16 * (lc ^ swz(row)) + 8 * (vq & 1);
+      for (int db = 0; db < 4; ++db) {
+        const int lc = 4 * db + 2 * vg + (vq >> 1);
+        voff[ih][db] = row * kRowBytes + 16 * (lc ^ swz(row)) + 8 * (vq & 1);
+      }
     }
   }
 
-  float m_run[2] = {-INFINITY, -INFINITY};   // running max (natural units), drives the vote
-  float mb_ref[2] = {-INFINITY, -INFINITY};  // exponent reference, log2 units
-  float l[2] = {0.f, 0.f};
-  f32x16 oacc[4][2];
+  float m_run = -INFINITY;    // running max (natural units), drives the vote
+  float mb_ref = -INFINITY;   // exponent reference, log2 units
+  float l = 0.f;
+  f32x16 oacc[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][qs][r] = 0.f;
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   int nskip = 0;
 
-  auto compute_tile = [&](int kt, const unsigned char* kl, const unsigned char* vl) {
-    // ---- scores S^T = K Q^T (always computed) ----
-    f32x16 sacc[4][2];
+  // per-tile state carried from C1 to C2
+  f32x16 sacc[4];
+  float tmax = 0.f;
+  bool own_pass = true;
+
+  // C1: scores S^T = K Q^T for tile kt with the row maximum folded in, then
+  // this wave's half of the vote.  K fragments are read kPfK steps ahead of
+  // their MFMA; each 32-key block's maximum is taken while the next block's
+  // MFMAs run.
+  auto c1_scores = [&](int kt) __attribute__((always_inline)) {
+    const unsigned char* kl = lds_k[kt & 1];
+    constexpr int kPfK = 4;
+    auto kfrag = [&](int i) __attribute__((always_inline)) {
+      const int kb = i >> 3, s = i & 7;
+      const int off = kb * 32 * kRowBytes + krow * kRowBytes + 16 * ((2 * s + hf) ^ kswz);
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + off));
+    };
+    bf16x8 ring[kPfK];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int i = 0; i < kPfK; ++i) ring[i] = kfrag(i);
+    float mx = -INFINITY;
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
+    for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][qs][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int koff = krow * kRowBytes + 16 * ((2 * s + hf) ^ kswz);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + kb * 32 * kRowBytes + koff));
-        sacc[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][s], sacc[kb][0], 0, 0, 0);
-        sacc[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][s], sacc[kb][1], 0, 0, 0);
-      }
+    for (int i = 0; i < 32; ++i) {
+      const int kb = i >> 3, s = i & 7;
+      const bf16x8 a = ring[i % kPfK];
+      if (i + kPfK < 32) ring[i % kPfK] = kfrag(i + kPfK);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+      if (kb > 0)   // two elements of the previous block per step
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[kb - 1][2 * s], sacc[kb - 1][2 * s + 1]));
     }
-    // Keys past the end of the sequence score -inf.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sacc[3][r]);
+    __builtin_amdgcn_sched_group_barrier(0x100, kPfK, 0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kPfK < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    }
     if ((kt + 1) * kBK > S_b) {
+      // Keys past the end of the sequence score -inf; redo the maximum.
+      mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt * kBK + 32 * kb + 16 * (r >> 3) + 8 * hf + (r & 7);
-          if (key >= S_b) {
-            sacc[kb][0][r] = -INFINITY;
-            sacc[kb][1][r] = -INFINITY;
-          }
+          if (key >= S_b) sacc[kb][r] = -INFINITY;
+          mx = __builtin_elementwise_maximum(mx, sacc[kb][r]);
         }
     }
-
-    // ---- tile maximum per query row and the skip vote ----
-    float tmax[2];
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      float mx = sacc[0][qs][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qs][r]);
-      tmax[qs] = scaled_max(halves_max(mx), p.scale);
-    }
-    const float d0 = vote_margin(tmax[0], m_run[0]);
-    const float d1 = vote_margin(tmax[1], m_run[1]);
-    const bool pass = (!valid0 || d0 < ln_lambda) && (!valid1 || d1 < ln_lambda);
-    const bool skip = vote && (__builtin_amdgcn_ballot_w64(!pass) == 0);
-
+    // this wave's half of the vote: every valid row passes
+    tmax = scaled_max(halves_max(mx), p.scale);
+    const float dmargin = vote_margin(tmax, m_run);
+    own_pass = __builtin_amdgcn_ballot_w64(valid && !(dmargin < ln_lambda)) == 0;
+    if (lane == 0) vote_lds[wave] = own_pass ? 1 : 0;
     if constexpr (kDebug) {
-      float md = fmaxf(valid0 ? d0 : -INFINITY, valid1 ? d1 : -INFINITY);
+      float md = valid ? dmargin : -INFINITY;
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) md = fmaxf(md, __shfl_xor(md, off));
-      if (lane == 0) {
+      if (lane == 0) margin_lds[wave] = md;
+    }
+  };
+
+  // P = exp(s - r) of 32-key block kb in bf16 ([t2] B operands) + row sum.
+  auto exp_block = [&](int kb, u32x4 (&pk)[2], float& rs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int r = 8 * t2 + 2 * w;
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2e, -mb_ref));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.scale_log2e, -mb_ref));
+        rs += e0 + e1;
+        pk[t2][w] = pack_bf16(e0, e1);
+      }
+  };
+
+  // C2: the vote group's decision; kept tiles: online-softmax update and
+  // O^T += V^T P^T.  Step j = (kb, t2, db) of the P.V product has its two
+  // transpose reads issued kPfV steps ahead; the exponentials of block kb + 1
+  // run while the MFMAs of block kb do.
+  auto c2_softmax_pv = [&](int kt) __attribute__((always_inline)) {
+    const bool partner_pass = vote_lds[wave ^ 1] != 0;
+    const bool skip = vote && own_pass && partner_pass;
+    if constexpr (kDebug) {
+      if (lane == 0 && (wave & 1) == 0) {
         const long long nqb = (S_b + kBQ - 1) / kBQ;
-        const long long idx = (((long long)b * p.H + h) * nqb + qb) * nkt + kt;
-        if (p.mask != nullptr) p.mask[idx] = skip ? 1 : 0;
-        if (p.margin != nullptr) p.margin[idx] = md;
+        if (qb < nqb) {
+          const long long idx = (((long long)b * p.H + h) * nqb + qb) * nkt + kt;
+          if (p.mask != nullptr) p.mask[idx] = skip ? 1 : 0;
+          if (p.margin != nullptr) p.margin[idx] = fmaxf(margin_lds[wave], margin_lds[wave + 1]);
+        }
       }
     }
-
     if (skip) {
       ++nskip;
       return;
     }
-
-    // ---- kept tile: online-softmax update ----
-    bool grow = false;
+    m_run = fmaxf(m_run, tmax);
+    if (__builtin_amdgcn_ballot_w64(m_run * kLog2e > mb_ref + kRescaleLog2) != 0) {
+      const float nb = m_run * kLog2e;
+      const float alpha = __builtin_amdgcn_exp2f(mb_ref - nb);   // 0 on the first kept tile
+      mb_ref = nb;
+      l *= alpha;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      m_run[qs] = fmaxf(m_run[qs], tmax[qs]);
-      grow |= m_run[qs] * kLog2e > mb_ref[qs] + kRescaleLog2;
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const unsigned char* vl = lds_v[kt & 1];
+    constexpr int kPfV = 6;
+    auto vfrag = [&](int j) __attribute__((always_inline)) {
+      const int kb = j >> 3, t2 = (j >> 2) & 1, db = j & 3;
+      const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
+      return __builtin_bit_cast(bf16x8, av);
+    };
+    bf16x8 ring[kPfV];
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const float nb = m_run[qs] * kLog2e;
-        const float alpha = __builtin_amdgcn_exp2f(mb_ref[qs] - nb);   // 0 on the first kept tile
-        mb_ref[qs] = nb;
-        l[qs] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][qs][r] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qs][r], p.scale_log2e, -mb_ref[qs]));
-          sacc[kb][qs][r] = e;
-          rs += e;
-        }
-      l[qs] += rs;
-    }
-    // ---- O^T += V^T P^T ----
+    for (int j = 0; j < kPfV; ++j) ring[j] = vfrag(j);
+    float rs = 0.f;
+    u32x4 pk[2][2];
+    exp_block(0, pk[0], rs);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      if (kb < 3) exp_block(kb + 1, pk[(kb + 1) & 1], rs);
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        u32x4 p0, p1;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          p0[w] = pack_bf16(sacc[kb][0][8 * t2 + 2 * w], sacc[kb][0][8 * t2 + 2 * w + 1]);
-          p1[w] = pack_bf16(sacc[kb][1][8 * t2 + 2 * w], sacc[kb][1][8 * t2 + 2 * w + 1]);
-        }
-        const bf16x8 pf0 = __builtin_bit_cast(bf16x8, p0), pf1 = __builtin_bit_cast(bf16x8, p1);
-        const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
-          u32x4 av;
-          av[0] = __builtin_bit_cast(u32x2, lo)[0];
-          av[1] = __builtin_bit_cast(u32x2, lo)[1];
-          av[2] = __builtin_bit_cast(u32x2, hi)[0];
-          av[3] = __builtin_bit_cast(u32x2, hi)[1];
-          const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-          oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf0, oacc[db][0], 0, 0, 0);
-          oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf1, oacc[db][1], 0, 0, 0);
-        }
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = 8 * kb + jj, t2 = jj >> 2, db = jj & 3;
+        const bf16x8 a = ring[j % kPfV];
+        if (j + kPfV < 32) ring[j % kPfV] = vfrag(j + kPfV);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[kb & 1][t2]), oacc[db], 0, 0, 0);
       }
     }
+    l += rs;
   };
 
-  // ---- main loop: two tiles per trip so both LDS buffers are static ----
-  issue_tile(0, lds_k0, lds_v0);
+  // ---- main loop over slots; each slot ends with a workgroup barrier ----
+  // Group A runs C1 of tile slot / 2 on even slots and C2 on odd slots;
+  // group B runs what A ran one slot earlier.  K(u + 1) is copied at slot 2u
+  // (its buffer was last read at slot 2u - 1), V(u + 1) at slot 2u + 1 (last
+  // read at 2u); each copy is waited for one slot later.
+  issue_copy(rk, 0, lds_k[0]);
+  issue_copy(rv, 0, lds_v[0]);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    if (kt + 1 < nkt) issue_tile(kt + 1, lds_k1, lds_v1);
-    if (wave_active) compute_tile(kt, lds_k0, lds_v0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (kt + 1 >= nkt) break;
-    if (kt + 2 < nkt) issue_tile(kt + 2, lds_k0, lds_v0);
-    if (wave_active) compute_tile(kt + 1, lds_k1, lds_v1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+  const int nslots = 2 * nkt + 1;
+  for (int slot = 0; slot < nslots; ++slot) {
+    const int u = slot >> 1;
+    if (u + 1 < nkt) {
+      if ((slot & 1) == 0)
+        issue_copy(rk, u + 1, lds_k[(u + 1) & 1]);
+      else
+        issue_copy(rv, u + 1, lds_v[(u + 1) & 1]);
+    }
+    const int my = group_b ? slot - 1 : slot;   // this group's own slot counter
+    if (my >= 0 && (my >> 1) < nkt) {
+      if ((my & 1) == 0)
+        c1_scores(my >> 1);
+      else
+        c2_softmax_pv(my >> 1);
+    }
+    // The copy issued in the previous slot must have landed before the next.
+    if constexpr (kDebug)
+      __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): debug stores share the counter
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopyPerWave);   // vmcnt(<= kCopyPerWave)
     __syncthreads();
   }
-
-  if (!wave_active) return;
 
   // ---- epilogue: O / l in bf16, LSE = r + ln l, skipped-tile count ----
   long long T = 0, qb_total = 0, qb_off = 0;
@@ -401,31 +434,29 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_fwd_kernel(const Params p) {
   }
   uint16_t* __restrict__ op = p.o + base;
   const long long ts = p.tok_stride;
+  const float lt = halves_sum(l);
+  const float inv = 1.f / lt;
+  const int row = wrow0 + c;
+  if (row < S_b) {
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    const float lt = halves_sum(l[qs]);
-    const float inv = 1.f / lt;
-    const int row = wrow0 + 32 * qs + c;
-    if (row < S_b) {
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 w;
-          w.x = pack_bf16(oacc[db][qs][4 * g] * inv, oacc[db][qs][4 * g + 1] * inv);
-          w.y = pack_bf16(oacc[db][qs][4 * g + 2] * inv, oacc[db][qs][4 * g + 3] * inv);
-          *reinterpret_cast<uint2*>(op + (long long)row * ts + 32 * db + 8 * g + 4 * hf) = w;
-        }
-      if (p.lse != nullptr && hf == 0) {
-        const float lse = mb_ref[qs] * (1.f / kLog2e) + logf(lt);
-        if (p.cu_seqlens != nullptr)
-          p.lse[(long long)h * T + tok0 + row] = lse;
-        else
-          p.lse[((long long)b * p.H + h) * p.S + row] = lse;
+      for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+        w.y = pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(op + (long long)row * ts + 32 * db + 8 * g + 4 * hf) = w;
       }
+    if (p.lse != nullptr && hf == 0) {
+      const float lse = mb_ref * (1.f / kLog2e) + logf(lt);
+      if (p.cu_seqlens != nullptr)
+        p.lse[(long long)h * T + tok0 + row] = lse;
+      else
+        p.lse[((long long)b * p.H + h) * p.S + row] = lse;
     }
   }
-  if (p.counts != nullptr && lane == 0) {
+  const long long nqb_seq = (S_b + kBQ - 1) / kBQ;
+  if (p.counts != nullptr && lane == 0 && (wave & 1) == 0 && qb < nqb_seq) {
     if (p.cu_seqlens != nullptr) {
       p.counts[(long long)h * qb_total + qb_off + qb] = nskip;
     } else {
