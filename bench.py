@@ -90,6 +90,19 @@ def cpu_baseline(w, ln_lambda, seconds):
                       f"float64 numpy recurrence, {dt:.1f} s"}
 
 
+def copy_reference(launches):
+    """A plain elementwise copy of known size (512 MiB read, 512 MiB written):
+    the rocprofv3 FETCH_SIZE / WRITE_SIZE it reports calibrate those counters."""
+    import torch
+    x = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": "copy", "bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +111,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--target", type=float, default=0.75, help="skip fraction of the timed step")
+    ap.add_argument("--counters", choices=("dense", "skip", "copy"), default=None,
+                    help="launch only one configuration (or the plain copy reference), for rocprofv3 --pmc")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -111,6 +126,10 @@ def main():
     import skip_softmax_flashattention_amd as ssa
     from skip_softmax_flashattention_amd import inputs
 
+    if args.counters == "copy":
+        copy_reference(args.steps)
+        return
+
     ssa.device_check()
     dev = torch.device("cuda:0")
     with open(os.path.join(ROOT, "tests", "golden", "wan_lambdas.json")) as f:
@@ -120,6 +139,16 @@ def main():
     B, H, S, D = q.shape
     factor = lam * S
     dense_flops = 4.0 * B * H * S * S * D
+
+    if args.counters is not None:
+        # Only the requested configuration: warmup + steps launches of one kernel.
+        f = 0.0 if args.counters == "dense" else factor
+        for _ in range(args.warmup + args.steps):
+            ssa.fwd(q, k, v, factor=f, scale=w.scale)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": args.counters, "launches": args.warmup + args.steps,
+                          "kernel_sha256_16": kernel_hash()}), flush=True)
+        return
 
     # Tile decisions of the timed configuration (debug entry point, outside the timed region).
     _, _, cnt_dbg, mask, _ = ssa.fwd_debug(q, k, v, factor=factor, scale=w.scale)

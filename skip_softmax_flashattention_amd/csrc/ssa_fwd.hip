@@ -139,9 +139,13 @@ __device__ __forceinline__ float vote_margin(float tile_max, float m) {
   return tile_max - m;
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -251,42 +255,41 @@ void ssa_fwd_kernel(const Params p) {
   float tmax = 0.f;
   bool own_pass = true;
 
-  // C1: scores S^T = K Q^T for tile kt with the row maximum folded in, then
-  // this wave's half of the vote.  K fragments are read kPfK steps ahead of
-  // their MFMA; each 32-key block's maximum is taken while the next block's
-  // MFMAs run.
+  // C1: scores S^T = K Q^T for tile kt with the row maximum, then this
+  // wave's half of the vote.  The MFMAs run channel step by channel step
+  // over the four 32-key blocks, so four independent accumulation chains
+  // hide the MFMA latency; K fragments are read kPfK MFMAs ahead.
   auto c1_scores = [&](int kt) __attribute__((always_inline)) {
     const unsigned char* kl = lds_k[kt & 1];
-    constexpr int kPfK = 4;
+    constexpr int kPfK = 6;
     auto kfrag = [&](int i) __attribute__((always_inline)) {
-      const int kb = i >> 3, s = i & 7;
+      const int s = i >> 2, kb = i & 3;
       const int off = kb * 32 * kRowBytes + krow * kRowBytes + 16 * ((2 * s + hf) ^ kswz);
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + off));
     };
     bf16x8 ring[kPfK];
 #pragma unroll
     for (int i = 0; i < kPfK; ++i) ring[i] = kfrag(i);
-    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const int kb = i >> 3, s = i & 7;
+      const int s = i >> 2, kb = i & 3;
       const bf16x8 a = ring[i % kPfK];
       if (i + kPfK < 32) ring[i % kPfK] = kfrag(i + kPfK);
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-      if (kb > 0)   // two elements of the previous block per step
-        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sacc[kb - 1][2 * s], sacc[kb - 1][2 * s + 1]));
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sacc[3][r]);
     __builtin_amdgcn_sched_group_barrier(0x100, kPfK, 0);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i + kPfK < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sacc[kb][r]);
     if ((kt + 1) * kBK > S_b) {
       // Keys past the end of the sequence score -inf; redo the maximum.
       mx = -INFINITY;
@@ -331,8 +334,25 @@ void ssa_fwd_kernel(const Params p) {
   // transpose reads issued kPfV steps ahead; the exponentials of block kb + 1
   // run while the MFMAs of block kb do.
   auto c2_softmax_pv = [&](int kt) __attribute__((always_inline)) {
-    const bool partner_pass = vote_lds[wave ^ 1] != 0;
-    const bool skip = vote && own_pass && partner_pass;
+    // The partner's vote and the first V fragments are requested together,
+    // before the decision, so their LDS latencies overlap (a skipped tile
+    // simply drops the fragments).
+    const unsigned char* vl = lds_v[kt & 1];
+    constexpr int kPfV = 6;
+    auto vfrag = [&](int j) __attribute__((always_inline)) {
+      const int kb = j >> 3, t2 = (j >> 2) & 1, db = j & 3;
+      const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
+      return __builtin_bit_cast(bf16x8, av);
+    };
+    const int partner_vote = vote_lds[wave ^ 1];
+    bf16x8 ring[kPfV];
+#pragma unroll
+    for (int j = 0; j < kPfV; ++j) ring[j] = vfrag(j);
+    const bool skip = vote && own_pass && partner_vote != 0;
     if constexpr (kDebug) {
       if (lane == 0 && (wave & 1) == 0) {
         const long long nqb = (S_b + kBQ - 1) / kBQ;
@@ -358,20 +378,6 @@ void ssa_fwd_kernel(const Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    const unsigned char* vl = lds_v[kt & 1];
-    constexpr int kPfV = 6;
-    auto vfrag = [&](int j) __attribute__((always_inline)) {
-      const int kb = j >> 3, t2 = (j >> 2) & 1, db = j & 3;
-      const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
-      return __builtin_bit_cast(bf16x8, av);
-    };
-    bf16x8 ring[kPfV];
-#pragma unroll
-    for (int j = 0; j < kPfV; ++j) ring[j] = vfrag(j);
     float rs = 0.f;
     u32x4 pk[2][2];
     exp_block(0, pk[0], rs);
