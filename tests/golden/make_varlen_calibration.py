@@ -1,0 +1,122 @@
+"""Fit the calibration coefficients (a, b) of the calibrated varlen workload.
+
+The calibrated control sets factor = a * exp(b * target_sparsity) and
+lambda_b = factor / S_b per sequence ("Skip-Softmax" design document of
+vLLM-Omni, section "From configuration to the kernel threshold").  The pages
+say the coefficients are fitted per model but give no procedure, so the
+reading taken here is an ordinary least-squares fit of
+
+    ln(factor) = ln(a) + b * s
+
+over a log-spaced sweep of factor, where s is the skipped-tile fraction that
+the CPU oracle reaches on each sequence of a calibration batch.  The batch has
+the same shape as the measured one (3 sequences of 4096, 16384 and 32760
+tokens, H = 16, grid-local generator) but a different seed (5 instead of 4).
+Points with 0.02 < s < 0.98 from all three sequences are pooled.
+
+The skip fraction at one factor comes from the oracle only:
+  * lambda_b <= 1: the closed-form prefix-maximum margins
+    (oracle.prefix_max_margins_head) of 16 seeded query blocks per head;
+  * lambda_b > 1 (decisions cascade): the recurrence itself
+    (oracle.skip_head) on 4 seeded query blocks of each of 8 seeded heads.
+
+Writes tests/golden/varlen_calibration.json.
+Run: python tests/golden/make_varlen_calibration.py
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import oracle  # noqa: E402
+from skip_softmax_flashattention_amd import inputs  # noqa: E402
+
+FIT_SEED = 5
+HEADS = 16
+TARGETS = (0.5, 0.7, 0.9)
+LOG2_FACTORS = [0.5 * i for i in range(0, 49)]   # factor = 2^0 .. 2^24
+S_LO, S_HI = 0.02, 0.98
+
+
+def per_sequence(w):
+    """[(S_b, q [H,S,D], k, v) float64] of a packed workload."""
+    out = []
+    for qs, ks, vs in zip(*(inputs.unpack_varlen(t, w.cu_seqlens) for t in (w.q, w.k, w.v))):
+        out.append((qs.shape[2], oracle.from_bf16(qs[0]), oracle.from_bf16(ks[0]), oracle.from_bf16(vs[0])))
+    return out
+
+
+def main():
+    t0 = time.time()
+    w = inputs.varlen(seed=FIT_SEED, heads=HEADS)
+    seqs = per_sequence(w)
+    rng = np.random.default_rng(4321)
+    points = []
+    detail = {}
+    for S, q, k, v in seqs:
+        nqb = -(-S // oracle.BLOCK_Q)
+        margins = np.concatenate([
+            oracle.prefix_max_margins_head(q[h], k[h], w.scale,
+                                           qblocks=np.sort(rng.choice(nqb, min(16, nqb), replace=False)))
+            for h in range(HEADS)])
+        heads = np.sort(rng.choice(HEADS, 8, replace=False))
+        units = [(h, np.sort(rng.choice(nqb, 4, replace=False))) for h in heads]
+
+        def frac_recurrence(ln_lam):
+            tot = sk = 0
+            for h, qbs in units:
+                r = oracle.skip_head(q[h], k[h], v[h], w.scale, ln_lam, qblocks=qbs)
+                tot += r.skipped.size
+                sk += int(r.skipped.sum())
+            return sk / tot
+
+        rows = []
+        for e in LOG2_FACTORS:
+            factor = 2.0 ** e
+            lam = oracle.resolve_lambda(factor=factor, seqlen=S)
+            ln = oracle.ln_lambda_f32(lam)
+            if lam <= 1.0:
+                s = float((margins < ln).mean())
+                how = "closed form"
+            else:
+                s = frac_recurrence(ln)
+                how = "recurrence"
+            rows.append({"factor": factor, "lambda": lam, "skip": s, "method": how})
+            if S_LO < s < S_HI:
+                points.append((s, math.log(factor)))
+            print(f"S={S:6d} factor 2^{e:4.1f} lambda {lam:.4g}: skip {s:.4f} ({how})", flush=True)
+            if s >= S_HI:
+                break
+        detail[str(S)] = rows
+    x = np.array([p[0] for p in points])
+    y = np.array([p[1] for p in points])
+    b = float(((x - x.mean()) * (y - y.mean())).sum() / ((x - x.mean()) ** 2).sum())
+    ln_a = float(y.mean() - b * x.mean())
+    a = math.exp(ln_a)
+    resid = y - (ln_a + b * x)
+    out = {
+        "workload": "calibration batch: varlen S = 4096, 16384, 32760 (grids 4x32x32, 16x32x32, 21x30x52), "
+                    f"H = {HEADS}, D = 128, seed {FIT_SEED}",
+        "fit": "OLS of ln(factor) on skipped-tile fraction, points with 0.02 < s < 0.98 pooled over sequences",
+        "a": a, "b": b, "n_points": len(points), "rms_residual_ln_factor": float(np.sqrt((resid ** 2).mean())),
+        "factor_at_target": {str(t): a * math.exp(b * t) for t in TARGETS},
+        "sweep": detail,
+        "seconds": round(time.time() - t0, 1),
+    }
+    with open(os.path.join(HERE, "varlen_calibration.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(f"a = {a:.6g}, b = {b:.6g} from {len(points)} points; factor at targets "
+          f"{ {t: round(a * math.exp(b * t), 2) for t in TARGETS} }", flush=True)
+
+
+if __name__ == "__main__":
+    main()
