@@ -243,6 +243,23 @@ def pin_omitted_mass(orc):
     assert (diff <= 2 * om * np.abs(v).max() + 1e-12).all()
 
 
+def pin_max_weight_is_inverse_l(orc):
+    """The largest softmax weight of a row over the keys that were accumulated
+    is exp(m - LSE) = 1/l, so it lies in [1/n_kept, 1] with m the largest kept
+    score, found here by brute force from the mask."""
+    q, k, v = _peaky_head(23, 96, 8, gain=4.0)
+    scale = 0.5
+    for lam in (0.0, 0.05, 0.3):
+        r = orc.skip_head(q, k, v, scale, orc.ln_lambda_f32(lam), block_q=8, block_k=16)
+        lse = r.lse.reshape(-1)
+        for i in range(96):
+            kept = [c for c in range(96) if not r.skipped[i // 8, c // 16]]
+            s = [scale * float(np.dot(q[i], k[c])) for c in kept]
+            w = math.exp(max(s) - lse[i])
+            assert 1.0 / len(kept) - 1e-12 <= w <= 1.0 + 1e-12, (lam, i, w)
+            assert abs(w - 1.0 / sum(math.exp(x - max(s)) for x in s)) < 1e-12
+
+
 def pin_planted_dominant_key(orc):
     """A key in tile 0 that beats every other key of every row of a query
     block by more than -ln(lambda) makes every later tile skippable; the
