@@ -159,9 +159,12 @@ void ssa_fwd_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
   __shared__ int vote_lds[kWaves];
   __shared__ float margin_lds[kWaves];
+  __shared__ uint32_t claim_lds[kWaves / 2];
 
   const int qg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int pair = wave & 3;   // waves pair and pair + 4 share a SIMD
   const int c = lane & 31, hf = lane >> 5;
   const bool group_b = wave >= 4;
 
@@ -202,22 +205,51 @@ void ssa_fwd_kernel(const Params p) {
   }
 
   // ---- tile copy: global -> LDS, 16 bytes per lane per instruction ----
-  // Instruction j of wave w fills LDS rows 4 (kCopyPerWave w + j) .. +3
-  // (1 KB); lane l lands at byte 16 l of that block: row 4 (..) + l / 16,
-  // physical chunk l % 16, which holds logical chunk (l % 16) ^ swz(row).
+  // The 128 rows of a tile are split in 8 blocks of 16 rows: block 4 hh + pair
+  // holds rows 16 (4 hh + pair) .. +15.  Instruction
+  // j of a block fills its rows 4 j .. 4 j + 3 (1 KB); lane l lands at byte
+  // 16 l: row + l / 16, physical chunk l % 16, which holds logical chunk
+  // (l % 16) ^ swz(row).  Rows 64 apart share a swizzle, so the two blocks of
+  // a pair differ by a uniform 64 rows.
   uint32_t copy_off[kCopyPerWave];
 #pragma unroll
   for (int j = 0; j < kCopyPerWave; ++j) {
-    const int r = 4 * (kCopyPerWave * wave + j) + (lane >> 4);
+    const int r = 4 * (kCopyPerWave * pair + j) + (lane >> 4);
     copy_off[j] = (uint32_t)r * ts_bytes + 16u * (uint32_t)((lane & 15) ^ swz(r));
   }
-  auto issue_copy = [&](const __amdgpu_buffer_rsrc_t& rs, int kt, unsigned char* dst) __attribute__((always_inline)) {
-    const uint32_t tile_off = (uint32_t)kt * kBK * ts_bytes;
+  auto copy_block = [&](const __amdgpu_buffer_rsrc_t& rs, int kt, unsigned char* dst, int hh) __attribute__((always_inline)) {
+    const uint32_t goff = (uint32_t)(kt * kBK + 64 * hh) * ts_bytes;
 #pragma unroll
-    for (int j = 0; j < kCopyPerWave; ++j) {
+    for (int j = 0; j < kCopyPerWave; ++j)
       // The whole offset goes in the per-lane (range-checked) voffset.
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, dst + 4 * (kCopyPerWave * wave + j) * kRowBytes),
-                                               16, copy_off[j] + tile_off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, LDS_PTR(void, dst + (4 * (kCopyPerWave * pair + j) + 64 * hh) * kRowBytes), 16, copy_off[j] + goff,
+          0, 0, 0);
+  };
+
+  // The copy of the current slot (tile u + 1, K on even slots, V on odd
+  // ones) is issued by one wave of each SIMD pair, for both: the two waves
+  // claim it through an LDS counter and the first claimer copies.  Both claim
+  // once in every slot that has a copy, so the first claimer of a slot reads
+  // an even count.  Each wave claims when its cluster is done, so the copy
+  // falls to the wave with slack: the score cluster when the tile is kept
+  // (the softmax cluster takes longer), the softmax cluster when the tile is
+  // skipped (it ends right after its decision).
+  bool cp_pending = false, cp_issued = false, cp_k = true;
+  int cp_tile = 0;
+  auto claim_copy = [&]() __attribute__((always_inline)) {
+    if (!cp_pending) return;
+    cp_pending = false;
+    uint32_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&claim_lds[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if ((old & 1u) == 0) {
+      unsigned char* dst = cp_k ? lds_k[cp_tile & 1] : lds_v[cp_tile & 1];
+      const __amdgpu_buffer_rsrc_t rs = cp_k ? rk : rv;
+      copy_block(rs, cp_tile, dst, 0);
+      copy_block(rs, cp_tile, dst, 1);
+      cp_issued = true;
     }
   };
 
@@ -400,19 +432,18 @@ void ssa_fwd_kernel(const Params p) {
   // group B runs what A ran one slot earlier.  K(u + 1) is copied at slot 2u
   // (its buffer was last read at slot 2u - 1), V(u + 1) at slot 2u + 1 (last
   // read at 2u); each copy is waited for one slot later.
-  issue_copy(rk, 0, lds_k[0]);
-  issue_copy(rv, 0, lds_v[0]);
+  copy_block(rk, 0, lds_k[0], wave >> 2);
+  copy_block(rv, 0, lds_v[0], wave >> 2);
+  if (tid < kWaves / 2) claim_lds[tid] = 0;
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   const int nslots = 2 * nkt + 1;
   for (int slot = 0; slot < nslots; ++slot) {
     const int u = slot >> 1;
-    if (u + 1 < nkt) {
-      if ((slot & 1) == 0)
-        issue_copy(rk, u + 1, lds_k[(u + 1) & 1]);
-      else
-        issue_copy(rv, u + 1, lds_v[(u + 1) & 1]);
-    }
+    cp_pending = u + 1 < nkt;
+    cp_issued = false;
+    cp_k = (slot & 1) == 0;
+    cp_tile = u + 1;
     const int my = group_b ? slot - 1 : slot;   // this group's own slot counter
     if (my >= 0 && (my >> 1) < nkt) {
       if ((my & 1) == 0)
@@ -420,12 +451,23 @@ void ssa_fwd_kernel(const Params p) {
       else
         c2_softmax_pv(my >> 1);
     }
-    // The copy issued in the previous slot must have landed before the next.
-    if constexpr (kDebug)
-      __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): debug stores share the counter
+    // The copy issued in the previous slot must have landed before the next;
+    // only this slot's own copy (the last kCopyPerWave memory operations) may
+    // remain in flight.
+    claim_copy();
+    // LDS operations (vote, operand reads) complete before the barrier, so the
+    // barrier orders them; a memory fence is not used because it would also
+    // wait for the copy still in flight.  Only this slot's own copy (the last
+    // 2 kCopyPerWave memory operations of the wave that issued it) may remain
+    // in flight: the previous slot's copy has landed everywhere after the
+    // barrier.
+    if (kDebug || !cp_issued)
+      __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) lgkmcnt(0) (debug stores share vmcnt)
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopyPerWave);   // vmcnt(<= kCopyPerWave)
-    __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0x0070 | 2 * kCopyPerWave);   // vmcnt(<= 2 kCopyPerWave) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // no compiler motion of memory operations across the barrier
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
 
   // ---- epilogue: O / l in bf16, LSE = r + ln l, skipped-tile count ----
