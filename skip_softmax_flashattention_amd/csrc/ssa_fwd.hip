@@ -50,6 +50,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 
 #include "ssa.h"
 
@@ -67,6 +68,7 @@ constexpr int kTileBytes = kBK * kRowBytes;        // 32 KB
 constexpr int kCopyPerWave = kTileBytes / (kWaves * 1024);   // 1 KB DMA instructions per wave per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 16.f;               // P <= 2^16 before a rescale is forced
+constexpr int kSpinLimit = 1 << 14;                 // polls of the partner's vote before giving up
 constexpr unsigned kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -157,14 +159,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void ssa_fwd_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
-  __shared__ int vote_lds[kWaves];
-  __shared__ float margin_lds[kWaves];
-  __shared__ uint32_t claim_lds[kWaves / 2];
+  __shared__ int vote_lds[kWaves];      // (tile << 1) | pass of the wave's half of the vote
+  __shared__ float margin_lds[kWaves];  // debug: the wave's margin for the tile
 
   const int qg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = tid >> 6;
-  const int pair = wave & 3;   // waves pair and pair + 4 share a SIMD
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hf = lane >> 5;
   const bool group_b = wave >= 4;
 
@@ -205,52 +204,24 @@ void ssa_fwd_kernel(const Params p) {
   }
 
   // ---- tile copy: global -> LDS, 16 bytes per lane per instruction ----
-  // The 128 rows of a tile are split in 8 blocks of 16 rows: block 4 hh + pair
-  // holds rows 16 (4 hh + pair) .. +15.  Instruction
-  // j of a block fills its rows 4 j .. 4 j + 3 (1 KB); lane l lands at byte
-  // 16 l: row + l / 16, physical chunk l % 16, which holds logical chunk
-  // (l % 16) ^ swz(row).  Rows 64 apart share a swizzle, so the two blocks of
-  // a pair differ by a uniform 64 rows.
+  // Instruction j of a 16-row block fills its rows 4 j .. 4 j + 3 (1 KB);
+  // lane l lands at byte 16 l: row + l / 16, physical chunk l % 16, which
+  // holds logical chunk (l % 16) ^ swz(row).  Rows 16 apart share a swizzle,
+  // so the blocks of a wave differ by uniform offsets.
   uint32_t copy_off[kCopyPerWave];
 #pragma unroll
   for (int j = 0; j < kCopyPerWave; ++j) {
-    const int r = 4 * (kCopyPerWave * pair + j) + (lane >> 4);
+    const int r = 4 * j + (lane >> 4);
     copy_off[j] = (uint32_t)r * ts_bytes + 16u * (uint32_t)((lane & 15) ^ swz(r));
   }
-  auto copy_block = [&](const __amdgpu_buffer_rsrc_t& rs, int kt, unsigned char* dst, int hh) __attribute__((always_inline)) {
-    const uint32_t goff = (uint32_t)(kt * kBK + 64 * hh) * ts_bytes;
+  // The 16-row block `blk` (0..7) of tile kt into the LDS tile at dst.
+  auto copy_block = [&](const __amdgpu_buffer_rsrc_t& rs, int kt, unsigned char* dst, int blk) __attribute__((always_inline)) {
+    const uint32_t goff = (uint32_t)(kt * kBK + 16 * blk) * ts_bytes;
 #pragma unroll
     for (int j = 0; j < kCopyPerWave; ++j)
       // The whole offset goes in the per-lane (range-checked) voffset.
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, LDS_PTR(void, dst + (4 * (kCopyPerWave * pair + j) + 64 * hh) * kRowBytes), 16, copy_off[j] + goff,
-          0, 0, 0);
-  };
-
-  // The copy of the current slot (tile u + 1, K on even slots, V on odd
-  // ones) is issued by one wave of each SIMD pair, for both: the two waves
-  // claim it through an LDS counter and the first claimer copies.  Both claim
-  // once in every slot that has a copy, so the first claimer of a slot reads
-  // an even count.  Each wave claims when its cluster is done, so the copy
-  // falls to the wave with slack: the score cluster when the tile is kept
-  // (the softmax cluster takes longer), the softmax cluster when the tile is
-  // skipped (it ends right after its decision).
-  bool cp_pending = false, cp_issued = false, cp_k = true;
-  int cp_tile = 0;
-  auto claim_copy = [&]() __attribute__((always_inline)) {
-    if (!cp_pending) return;
-    cp_pending = false;
-    uint32_t old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(&claim_lds[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if ((old & 1u) == 0) {
-      unsigned char* dst = cp_k ? lds_k[cp_tile & 1] : lds_v[cp_tile & 1];
-      const __amdgpu_buffer_rsrc_t rs = cp_k ? rk : rv;
-      copy_block(rs, cp_tile, dst, 0);
-      copy_block(rs, cp_tile, dst, 1);
-      cp_issued = true;
-    }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, dst + (16 * blk + 4 * j) * kRowBytes), 16,
+                                               copy_off[j] + goff, 0, 0, 0);
   };
 
   // Per-lane LDS byte offsets of the operand reads.
@@ -282,41 +253,74 @@ void ssa_fwd_kernel(const Params p) {
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   int nskip = 0;
 
-  // per-tile state carried from C1 to C2
+  // Scores of the tile between its MFMA and softmax phases.  The softmax
+  // phase of a kept tile overwrites them in place with P in bf16: register
+  // 4 t2 + w of block kb holds the pair of keys 8 t2 + 2 w, + 1, and
+  // registers 4 t2 .. 4 t2 + 3 are the B operand (P^T) of P.V step (kb, t2).
   f32x16 sacc[4];
-  float tmax = 0.f;
-  bool own_pass = true;
+  bool p_ready = false;
 
-  // C1: scores S^T = K Q^T for tile kt with the row maximum, then this
-  // wave's half of the vote.  The MFMAs run channel step by channel step
-  // over the four 32-key blocks, so four independent accumulation chains
-  // hide the MFMA latency; K fragments are read kPfK MFMAs ahead.
-  auto c1_scores = [&](int kt) __attribute__((always_inline)) {
+  // ---- MFMA phase: O^T += V^T P^T for the previous tile (if kept), then
+  // S^T = K Q^T for tile kt.  One stream of up to 64 MFMAs whose A operands
+  // (V^T by transpose reads, then K) come from LDS through one ring of
+  // fragments read kRing steps ahead; four independent accumulators in each
+  // half hide the MFMA latency.
+  constexpr int kRing = 8;
+  auto mfma_phase = [&](auto pv_c, auto qk_c, int kt) __attribute__((always_inline)) {
+    constexpr bool kPV = decltype(pv_c)::value, kQK = decltype(qk_c)::value;
+    constexpr int n0 = kPV ? 0 : 32, n1 = kQK ? 64 : 32;   // steps [n0, n1): < 32 P.V, >= 32 QK^T
+    const unsigned char* vl = lds_v[(kt - 1) & 1];
     const unsigned char* kl = lds_k[kt & 1];
-    constexpr int kPfK = 6;
-    auto kfrag = [&](int i) __attribute__((always_inline)) {
-      const int s = i >> 2, kb = i & 3;
+    auto frag = [&](int i) __attribute__((always_inline)) {
+      if (i < 32) {
+        const int kb = i >> 3, t2 = (i >> 2) & 1, db = i & 3;
+        const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, av);
+      }
+      const int s = (i - 32) >> 2, kb = i & 3;
       const int off = kb * 32 * kRowBytes + krow * kRowBytes + 16 * ((2 * s + hf) ^ kswz);
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + off));
     };
-    bf16x8 ring[kPfK];
+    bf16x8 ring[kRing];
 #pragma unroll
-    for (int i = 0; i < kPfK; ++i) ring[i] = kfrag(i);
+    for (int i = 0; i < kRing; ++i) ring[i] = frag(n0 + i);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int s = i >> 2, kb = i & 3;
-      const bf16x8 a = ring[i % kPfK];
-      if (i + kPfK < 32) ring[i % kPfK] = kfrag(i + kPfK);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+    for (int i = n0; i < n1; ++i) {
+      const bf16x8 a = ring[(i - n0) % kRing];
+      if (i + kRing < n1) ring[(i - n0) % kRing] = frag(i + kRing);
+      if (i < 32) {
+        const int kb = i >> 3, t2 = (i >> 2) & 1, db = i & 3;
+        const u32x4 pb = {__float_as_uint(sacc[kb][4 * t2]), __float_as_uint(sacc[kb][4 * t2 + 1]),
+                          __float_as_uint(sacc[kb][4 * t2 + 2]), __float_as_uint(sacc[kb][4 * t2 + 3])};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pb), oacc[db], 0, 0, 0);
+      } else {
+        const int s = (i - 32) >> 2, kb = i & 3;
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, kPfK, 0);
+    // Keep the order: reads for step i + kRing go out right after MFMA i.
+    __builtin_amdgcn_sched_group_barrier(0x100, (kPV ? 2 : 1) * kRing, 0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = n0; i < n1; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + kPfK < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i + kRing < n1) {
+        if (i + kRing < 32)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
+  };
+
+  // ---- softmax phase of tile kt: row maximum, this wave's half of the
+  // vote, the vote group's decision (the partner wave runs the same phase in
+  // the same slot and publishes through LDS), and for a kept tile the
+  // online-softmax update with P = exp(s - r) packed to bf16.
+  auto softmax_phase = [&](int kt) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -334,69 +338,46 @@ void ssa_fwd_kernel(const Params p) {
           mx = __builtin_elementwise_maximum(mx, sacc[kb][r]);
         }
     }
-    // this wave's half of the vote: every valid row passes
-    tmax = scaled_max(halves_max(mx), p.scale);
+    const float tmax = scaled_max(halves_max(mx), p.scale);
     const float dmargin = vote_margin(tmax, m_run);
-    own_pass = __builtin_amdgcn_ballot_w64(valid && !(dmargin < ln_lambda)) == 0;
-    if (lane == 0) vote_lds[wave] = own_pass ? 1 : 0;
-    if constexpr (kDebug) {
-      float md = valid ? dmargin : -INFINITY;
+    bool skip = false;
+    if (vote || kDebug) {
+      const bool own_pass = __builtin_amdgcn_ballot_w64(valid && !(dmargin < ln_lambda)) == 0;
+      if constexpr (kDebug) {
+        float md = valid ? dmargin : -INFINITY;
 #pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) md = fmaxf(md, __shfl_xor(md, off));
-      if (lane == 0) margin_lds[wave] = md;
-    }
-  };
-
-  // P = exp(s - r) of 32-key block kb in bf16 ([t2] B operands) + row sum.
-  auto exp_block = [&](int kb, u32x4 (&pk)[2], float& rs) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int r = 8 * t2 + 2 * w;
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2e, -mb_ref));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.scale_log2e, -mb_ref));
-        rs += e0 + e1;
-        pk[t2][w] = pack_bf16(e0, e1);
+        for (int off = 16; off >= 1; off >>= 1) md = fmaxf(md, __shfl_xor(md, off));
+        if (lane == 0) margin_lds[wave] = md;
       }
-  };
-
-  // C2: the vote group's decision; kept tiles: online-softmax update and
-  // O^T += V^T P^T.  Step j = (kb, t2, db) of the P.V product has its two
-  // transpose reads issued kPfV steps ahead; the exponentials of block kb + 1
-  // run while the MFMAs of block kb do.
-  auto c2_softmax_pv = [&](int kt) __attribute__((always_inline)) {
-    // The partner's vote and the first V fragments are requested together,
-    // before the decision, so their LDS latencies overlap (a skipped tile
-    // simply drops the fragments).
-    const unsigned char* vl = lds_v[kt & 1];
-    constexpr int kPfV = 6;
-    auto vfrag = [&](int j) __attribute__((always_inline)) {
-      const int kb = j >> 3, t2 = (j >> 2) & 1, db = j & 3;
-      const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
-      return __builtin_bit_cast(bf16x8, av);
-    };
-    const int partner_vote = vote_lds[wave ^ 1];
-    bf16x8 ring[kPfV];
-#pragma unroll
-    for (int j = 0; j < kPfV; ++j) ring[j] = vfrag(j);
-    const bool skip = vote && own_pass && partner_vote != 0;
-    if constexpr (kDebug) {
-      if (lane == 0 && (wave & 1) == 0) {
-        const long long nqb = (S_b + kBQ - 1) / kBQ;
-        if (qb < nqb) {
-          const long long idx = (((long long)b * p.H + h) * nqb + qb) * nkt + kt;
-          if (p.mask != nullptr) p.mask[idx] = skip ? 1 : 0;
-          if (p.margin != nullptr) p.margin[idx] = fmaxf(margin_lds[wave], margin_lds[wave + 1]);
+      // The vote carries the tile index, so no reset is needed between tiles;
+      // the debug margin is published before it (release / acquire).
+      constexpr int kPub = kDebug ? __ATOMIC_RELEASE : __ATOMIC_RELAXED;
+      constexpr int kSub = kDebug ? __ATOMIC_ACQUIRE : __ATOMIC_RELAXED;
+      if (lane == 0)
+        __hip_atomic_store(&vote_lds[wave], (kt << 1) | (own_pass ? 1 : 0), kPub, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // The partner publishes in this same slot; the bound only guards
+      // against a wave that never arrives.
+      int pv = 0;
+      for (int spin = 0; spin < kSpinLimit; ++spin) {
+        pv = __hip_atomic_load(&vote_lds[wave ^ 1], kSub, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((pv >> 1) == kt) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      skip = vote && own_pass && (pv & 1) != 0;
+      if constexpr (kDebug) {
+        if (lane == 0 && (wave & 1) == 0) {
+          const long long nqb = (S_b + kBQ - 1) / kBQ;
+          if (qb < nqb) {
+            const long long idx = (((long long)b * p.H + h) * nqb + qb) * nkt + kt;
+            if (p.mask != nullptr) p.mask[idx] = skip ? 1 : 0;
+            if (p.margin != nullptr) p.margin[idx] = fmaxf(margin_lds[wave], margin_lds[wave + 1]);
+          }
         }
       }
     }
     if (skip) {
       ++nskip;
+      p_ready = false;
       return;
     }
     m_run = fmaxf(m_run, tmax);
@@ -411,60 +392,68 @@ void ssa_fwd_kernel(const Params p) {
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
     float rs = 0.f;
-    u32x4 pk[2][2];
-    exp_block(0, pk[0], rs);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (kb < 3) exp_block(kb + 1, pk[(kb + 1) & 1], rs);
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = 8 * kb + jj, t2 = jj >> 2, db = jj & 3;
-        const bf16x8 a = ring[j % kPfV];
-        if (j + kPfV < 32) ring[j % kPfV] = vfrag(j + kPfV);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[kb & 1][t2]), oacc[db], 0, 0, 0);
-      }
-    }
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r = 8 * t2 + 2 * w;
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2e, -mb_ref));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.scale_log2e, -mb_ref));
+          rs += e0 + e1;
+          sacc[kb][4 * t2 + w] = __uint_as_float(pack_bf16(e0, e1));
+        }
     l += rs;
+    p_ready = true;
   };
 
   // ---- main loop over slots; each slot ends with a workgroup barrier ----
-  // Group A runs C1 of tile slot / 2 on even slots and C2 on odd slots;
-  // group B runs what A ran one slot earlier.  K(u + 1) is copied at slot 2u
-  // (its buffer was last read at slot 2u - 1), V(u + 1) at slot 2u + 1 (last
-  // read at 2u); each copy is waited for one slot later.
-  copy_block(rk, 0, lds_k[0], wave >> 2);
-  copy_block(rv, 0, lds_v[0], wave >> 2);
-  if (tid < kWaves / 2) claim_lds[tid] = 0;
+  // Group A runs the MFMA phase of tile slot / 2 on even slots and its
+  // softmax phase on odd slots; group B runs what A ran one slot earlier.
+  // So on every SIMD one wave feeds the matrix cores while the other runs
+  // the softmax.  The MFMA phase of tile j reads K(j) and V(j - 1) in slots
+  // 2j (A) and 2j + 1 (B); group B copies K(j + 1) and V(j), into the other
+  // buffers, at the end of its softmax phase in slot 2j, and waits for them
+  // at the end of slot 2j + 1.
+  if (tid < kWaves) vote_lds[tid] = -2;
+  copy_block(rk, 0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  const int nslots = 2 * nkt + 1;
+  const int nslots = 2 * nkt + 2;
   for (int slot = 0; slot < nslots; ++slot) {
-    const int u = slot >> 1;
-    cp_pending = u + 1 < nkt;
-    cp_issued = false;
-    cp_k = (slot & 1) == 0;
-    cp_tile = u + 1;
     const int my = group_b ? slot - 1 : slot;   // this group's own slot counter
-    if (my >= 0 && (my >> 1) < nkt) {
-      if ((my & 1) == 0)
-        c1_scores(my >> 1);
-      else
-        c2_softmax_pv(my >> 1);
+    if (my >= 0) {
+      const int kt = my >> 1;
+      if ((my & 1) == 0) {
+        if (kt < nkt) {
+          if (p_ready)
+            mfma_phase(std::true_type{}, std::true_type{}, kt);
+          else
+            mfma_phase(std::false_type{}, std::true_type{}, kt);
+        } else if (p_ready) {
+          mfma_phase(std::true_type{}, std::false_type{}, kt);
+        }
+        p_ready = false;
+      } else if (kt < nkt) {
+        softmax_phase(kt);
+      }
     }
-    // The copy issued in the previous slot must have landed before the next;
-    // only this slot's own copy (the last kCopyPerWave memory operations) may
-    // remain in flight.
-    claim_copy();
-    // LDS operations (vote, operand reads) complete before the barrier, so the
-    // barrier orders them; a memory fence is not used because it would also
-    // wait for the copy still in flight.  Only this slot's own copy (the last
-    // 2 kCopyPerWave memory operations of the wave that issued it) may remain
-    // in flight: the previous slot's copy has landed everywhere after the
-    // barrier.
-    if (kDebug || !cp_issued)
-      __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) lgkmcnt(0) (debug stores share vmcnt)
+    if (group_b && (slot & 1) == 0) {
+      const int j = slot >> 1;
+      if (j + 1 < nkt) copy_block(rk, j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
+      if (j + 1 < nkt) copy_block(rk, j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
+      if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4));
+      if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4) + 1);
+    }
+    // LDS operations (votes, operand reads) complete before the barrier, so
+    // the barrier orders them; a memory fence is not used because it would
+    // also wait for copies still in flight.  Copies issued in an even slot
+    // are waited for at the end of the following odd slot.
+    if (kDebug || (slot & 1) != 0)
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     else
-      __builtin_amdgcn_s_waitcnt(0x0070 | 2 * kCopyPerWave);   // vmcnt(<= 2 kCopyPerWave) lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // no compiler motion of memory operations across the barrier
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
