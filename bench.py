@@ -60,7 +60,8 @@ def issued_mfma_flops(mask, D=128, bq=64, bk=128):
 
 
 def cpu_baseline(w, ln_lambda, seconds):
-    """The oracle's recurrence on q-blocks of head 0, sized to about ``seconds``."""
+    """The oracle's recurrence on seeded query blocks of the workload's heads
+    (whole heads in order, then part of the next), sized to about ``seconds``."""
     import numpy as np
     import oracle
     try:
@@ -68,26 +69,36 @@ def cpu_baseline(w, ln_lambda, seconds):
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
     except Exception:
         cores = os.cpu_count() or 1
-    qd, kd, vd = (oracle.from_bf16(t[0, 0]) for t in (w.q, w.k, w.v))
-    S = qd.shape[0]
-    rng = np.random.default_rng(7)
+    S = w.q.shape[2]
+    nqb = -(-S // 64)
+    c = np.minimum(128, S - 128 * np.arange(-(-S // 128))).astype(np.float64)
 
-    def run(n):
-        qbs = np.sort(rng.choice(-(-S // 64), n, replace=False))
+    def run_head(h, n, rng):
+        qd, kd, vd = (oracle.from_bf16(t[0, h]) for t in (w.q, w.k, w.v))
+        qbs = np.sort(rng.choice(nqb, n, replace=False))
         t0 = time.perf_counter()
         r = oracle.skip_head(qd, kd, vd, w.scale, ln_lambda, qblocks=qbs)
         dt = time.perf_counter() - t0
         rows = np.minimum(64, S - 64 * qbs).astype(np.float64)
-        c = np.minimum(128, S - 128 * np.arange(r.skipped.shape[1])).astype(np.float64)
-        fl = 2.0 * 128 * (rows[:, None] * c[None, :] * (1 + (~r.skipped))).sum()
-        return dt, fl
+        return dt, 2.0 * 128 * (rows[:, None] * c[None, :] * (1 + (~r.skipped))).sum()
 
-    dt, fl = run(2)
-    n = int(min(512, max(2, round(2 * seconds / max(dt, 1e-3)))))
-    dt, fl = run(n)
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of 512 query blocks (64 rows x all 256 key tiles) of head 0 at the same lambda; "
-                      f"float64 numpy recurrence, {dt:.1f} s"}
+    rng = np.random.default_rng(7)
+    dt0, _ = run_head(0, 2, rng)
+    per_block = dt0 / 2
+    budget = int(max(2, round(seconds / max(per_block, 1e-4))))
+    tot_dt = tot_fl = 0.0
+    heads = 0
+    while budget > 0 and heads < w.q.shape[1]:
+        n = min(nqb, budget)
+        dt, fl = run_head(heads, n, rng)
+        tot_dt += dt
+        tot_fl += fl
+        budget -= n
+        heads += 1
+    blocks = int(round(seconds / max(per_block, 1e-4)))
+    return {"value": round(tot_fl / tot_dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{min(blocks, nqb * heads)} query blocks (64 rows x all 256 key tiles) over the first {heads} "
+                      f"head(s), seeded, at the same lambda; float64 numpy recurrence, {tot_dt:.1f} s"}
 
 
 def copy_reference(launches):
@@ -190,6 +201,25 @@ def main():
     exe = exec_flops / (t_s * 1e-3) / 1e12
     dense_tf = dense_flops / (t_d * 1e-3) / 1e12
 
+    # One GPU's share of an 8-way head split (Ulysses-style): H = 5 at the same length.
+    q5, k5, v5 = (t[:, :5].contiguous() for t in (q, k, v))
+    for _ in range(2):
+        ssa.fwd(q5, k5, v5, factor=0.0, scale=w.scale)
+        ssa.fwd(q5, k5, v5, factor=factor, scale=w.scale)
+    torch.cuda.synchronize()
+    e5 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        e5[i][0].record(stream)
+        ssa.fwd(q5, k5, v5, factor=0.0, scale=w.scale)
+        e5[i][1].record(stream)
+        e5[i][2].record(stream)
+        ssa.fwd(q5, k5, v5, factor=factor, scale=w.scale)
+        e5[i][3].record(stream)
+    torch.cuda.synchronize()
+    d5 = float(np.mean([a[0].elapsed_time(a[1]) for a in e5]))
+    s5 = float(np.mean([a[2].elapsed_time(a[3]) for a in e5]))
+    del q5, k5, v5
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -237,6 +267,9 @@ def main():
             "tflop_per_call": round(dense_flops / 1e12, 4),
         },
         "speedup_vs_dense": round(t_d / t_s, 4),
+        "ulysses8_share": {"heads": 5, "dense_ms": round(d5, 4), "skip_ms": round(s5, 4),
+                           "dense_mfma_util": round(dense_flops / 8 / (d5 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "speedup_vs_dense": round(d5 / s5, 4)},
         "timed_wall_s": round(t_wall, 3),
         "kernel_sha256_16": kernel_hash(),
     }
