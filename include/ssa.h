@@ -63,7 +63,8 @@ typedef enum {
   SSA_ERR_BAD_THRESHOLD = -3,  /* factor / threshold / lambda negative or non-finite, seqlen <= 0 */
   SSA_ERR_NO_CALIBRATION = -4, /* calibrated call with a <= 0 or non-finite a, b: use the threshold entry */
   SSA_ERR_DEVICE = -5,         /* no HIP device, or the current device is not gfx950 */
-  SSA_ERR_LAUNCH = -6          /* the kernel launch failed */
+  SSA_ERR_LAUNCH = -6,         /* the kernel launch failed */
+  SSA_ERR_BAD_CONFIG = -7      /* a calibration formula other than a * exp(b * target_sparsity) */
 } ssa_status;
 
 /* Threshold controls of ssa_fwd_varlen and ssa_resolve_threshold. */
@@ -121,6 +122,58 @@ int ssa_fwd_debug(const void* q, const void* k, const void* v, void* o, float* l
  * length seqlen, and whether the test is on (lambda > 0).  No HIP call. */
 int ssa_resolve_threshold(int mode, double p0, double p1, double p2, int seqlen,
                           float* ln_lambda, int* vote_enabled);
+
+/* ---- Host-side configuration (no HIP call; "Skip-Softmax" design document
+ * of vLLM-Omni, sections "From configuration to the kernel threshold" and
+ * "Timestep gating").  A layer's factor for one attention call is resolved
+ * from the user control, the layer's calibration and the denoising step, and
+ * then passed to ssa_fwd (0 = dense). ---- */
+
+/* SSA_OK if formula is exactly "a * exp(b * target_sparsity)", the only
+ * accepted calibration curve, else SSA_ERR_BAD_CONFIG (reject at startup). */
+int ssa_check_formula(const char* formula);
+
+/* Startup check of the user control: exactly one of threshold and
+ * target_sparsity (else SSA_ERR_INVALID_ARG); a threshold finite and >= 0
+ * and a target finite (else SSA_ERR_BAD_THRESHOLD); a target needs a
+ * calibration in the checkpoint (has_calibration, else
+ * SSA_ERR_NO_CALIBRATION: use the threshold control instead). */
+int ssa_check_spec(int has_threshold, double threshold, int has_target, double target_sparsity,
+                   int has_calibration);
+
+/* *matched = 1 when one of the npatterns fnmatch patterns matches the full
+ * module name or the name relative to `component` (what follows
+ * "<component>."); such a layer gets no coefficients and stays dense.
+ * component may be NULL or empty. */
+int ssa_ignore_match(const char* module_name, const char* component, const char* const* patterns,
+                     int npatterns, int* matched);
+
+/* The factor one attention call hands to the kernel (*factor_out, 0 = run
+ * dense).  Control: threshold (factor = threshold * seqlen, i.e. lambda =
+ * threshold) or target_sparsity (factor = a * exp(b * target_sparsity) from
+ * the layer's coefficients; a layer without coefficients runs dense).  A
+ * layer matched by an ignore pattern (ignored = 1) runs dense under either
+ * control.
+ * Timestep gate: disabled_until_timestep = 0 turns it off (t not read); a
+ * positive cutoff D runs the call dense while t > D or when no t is
+ * published (has_t = 0).  Errors: both or neither control
+ * (SSA_ERR_INVALID_ARG); a negative or non-finite threshold, target, cutoff
+ * or seqlen <= 0 (SSA_ERR_BAD_THRESHOLD); coefficients with a <= 0 or
+ * non-finite (SSA_ERR_NO_CALIBRATION). */
+int ssa_layer_factor(int has_threshold, double threshold, int has_target, double target_sparsity,
+                     int ignored, int has_coefficients, double a, double b, int seqlen, int has_t,
+                     double t, double disabled_until_timestep, double* factor_out);
+
+/* *count = number of the n published timesteps t[i] above the cutoff, i.e.
+ * the denoising steps that run dense (0 when the cutoff is 0). */
+int ssa_dense_steps(const double* t, int n, double disabled_until_timestep, int* count);
+
+/* Published timesteps of a flow-shifted rectified-flow schedule:
+ * num_inference_steps uniform positions u from 1 to 0 mapped to
+ * t = shift u / (1 + (shift - 1) u); t_out receives the first
+ * num_inference_steps - 1 (one per denoiser forward).  shift > 0,
+ * num_inference_steps >= 2. */
+int ssa_flow_shift_schedule(double shift, int num_inference_steps, double* t_out);
 
 /* SSA_OK when the current HIP device is gfx950. */
 int ssa_device_check(void);

@@ -2,7 +2,8 @@
 
     python -m skip_softmax_flashattention_amd.build
 
-compiles csrc/ssa_fwd.hip into _lib/libssa.so with hipcc.  The library is
+compiles csrc/ssa_fwd.hip (kernels and their C ABI) and csrc/ssa_config.cpp
+(host-only configuration helpers) into _lib/libssa.so with hipcc.  The library is
 rebuilt every time this runs.
 """
 from __future__ import annotations
@@ -15,6 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "ssa_fwd.hip")
+SRC_HOST = os.path.join(PKG, "csrc", "ssa_config.cpp")   # host-only configuration helpers
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 OUT = os.path.join(OUT_DIR, "libssa.so")
@@ -33,7 +35,7 @@ def command() -> list:
         "-I" + INCLUDE,
         # no packed fp32 instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-o", OUT + ".tmp", SRC,
+        "-o", OUT + ".tmp", SRC, SRC_HOST,
     ]
 
 

@@ -732,6 +732,7 @@ const char* ssa_strerror(int status) {
     case SSA_ERR_NO_CALIBRATION: return "SSA_ERR_NO_CALIBRATION: missing calibration, use the threshold entry";
     case SSA_ERR_DEVICE: return "SSA_ERR_DEVICE: no gfx950 device";
     case SSA_ERR_LAUNCH: return "SSA_ERR_LAUNCH: kernel launch failed";
+    case SSA_ERR_BAD_CONFIG: return "SSA_ERR_BAD_CONFIG: unsupported calibration formula";
     default: return "unknown ssa_status";
   }
 }
