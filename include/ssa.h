@@ -108,6 +108,18 @@ int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
                    float scale, int mode, double p0, double p1, double p2,
                    int32_t* skip_counts, void* stream);
 
+/* Any of the three controls (see ssa_mode; S_b = seqlen), with the largest
+ * softmax weight of every row as an extra output: max_prob float [B, H, S]
+ * (nullable), max_prob_i = exp(m_i - LSE_i) = 1 / l_i with l_i the row's
+ * denominator relative to its maximum m_i over the kept keys; near 1 for a
+ * row dominated by one key, near 1/N for a flat row (video-attention blog
+ * post on Wan 2.2, section "max_prob = 1 / l_i, and why it is free").  It
+ * comes from the epilogue at no extra pass over memory; the other outputs
+ * are those of ssa_fwd. */
+int ssa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int S, int D, float scale, int mode, double p0, double p1, double p2,
+               int seqlen, int32_t* skip_counts, float* max_prob, void* stream);
+
 /* Any of the three controls (see ssa_mode; S_b = seqlen) with every tile
  * decision reported: tile_mask uint8 [B, H, ceil(S/64), ceil(S/128)]
  * (1 = skipped) and tile_margin float (same shape, nullable): the largest

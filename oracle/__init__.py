@@ -22,4 +22,5 @@ from .skip_attention import (  # noqa: F401
     skip_attention_varlen,
     skip_head,
     skipped_mass_head,
+    max_prob_head,
 )

@@ -309,6 +309,29 @@ def skipped_mass_head(q: np.ndarray, k: np.ndarray, scale: float, skipped: np.nd
     return out
 
 
+def max_prob_head(q: np.ndarray, k: np.ndarray, scale: float, skipped: np.ndarray, lse: np.ndarray,
+                  qblocks: Optional[Iterable[int]] = None,
+                  block_q: int = BLOCK_Q, block_k: int = BLOCK_K) -> np.ndarray:
+    """The largest softmax weight of each row over the keys of its block's
+    kept tiles: exp(max kept score - LSE_i), which equals 1 / l_i with l_i
+    the row sum taken relative to the kept maximum (video-attention blog
+    post on Wan 2.2, section "max_prob = 1 / l_i, and why it is free").
+
+    skipped: [nb, nKT] decisions of the listed q-blocks (all by default);
+    lse: [nb, block_q] as returned with them.  Returns [nb, block_q]
+    (padding rows -inf)."""
+    S = q.shape[0]
+    qbs = np.arange(-(-S // block_q)) if qblocks is None else np.asarray(list(qblocks))
+    key_tile = np.arange(S) // block_k
+    out = np.full((len(qbs), block_q), -np.inf)
+    for j, qb in enumerate(qbs):
+        r0, r1 = int(qb) * block_q, min(S, (int(qb) + 1) * block_q)
+        s = float(scale) * (q[r0:r1] @ k.T)
+        kept = ~skipped[j][key_tile]
+        out[j, : r1 - r0] = np.exp(s[:, kept].max(axis=1) - lse[j, : r1 - r0])
+    return out
+
+
 def lambda_for_skip_fraction(margins: np.ndarray, fraction: float) -> float:
     """Smallest lambda <= 1 whose skip mask, from prefix-maximum margins,
     covers at least ``fraction`` of all tiles; ``margin < ln(lambda)`` skips

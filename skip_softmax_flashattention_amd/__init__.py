@@ -69,8 +69,9 @@ def load_library() -> ctypes.CDLL:
     lib.ssa_fwd_calibrated.argtypes = [P, P, P, P, P, I, I, I, I, F, F, F, F, I, P, P]
     lib.ssa_fwd_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, D, D, D, P, P]
     lib.ssa_fwd_debug.argtypes = [P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, P, P]
+    lib.ssa_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, P]
     lib.ssa_resolve_threshold.argtypes = [I, D, D, D, I, ctypes.POINTER(F), ctypes.POINTER(I)]
-    for name in ("ssa_fwd", "ssa_fwd_threshold", "ssa_fwd_calibrated", "ssa_fwd_varlen", "ssa_fwd_debug",
+    for name in ("ssa_fwd", "ssa_fwd_threshold", "ssa_fwd_calibrated", "ssa_fwd_varlen", "ssa_fwd_debug", "ssa_fwd_ex",
                  "ssa_resolve_threshold", "ssa_device_check", "ssa_version"):
         getattr(lib, name).restype = I
     lib.ssa_device_check.argtypes = []
@@ -178,6 +179,27 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
                             int(max_seqlen), H, D, scale, mode, p0, p1, p2, _ptr(cnt), _stream(q))
     _check(rc)
     return o, lse, cnt
+
+
+def fwd_max_prob(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+                 factor: Optional[float] = None, threshold: Optional[float] = None, calib=None,
+                 seqlen: Optional[int] = None):
+    """fwd plus each row's largest softmax weight over the kept keys,
+    max_prob = exp(m - LSE) = 1 / l: returns (o, lse, skip_counts, max_prob
+    float32 [B, H, S])."""
+    _check_qkv(q, k, v, 4)
+    B, H, S, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    mode, p0, p1, p2 = _control(factor, threshold, calib)
+    n = S if seqlen is None else int(seqlen)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    cnt = torch.empty((B, H, -(-S // BLOCK_Q)), dtype=torch.int32, device=q.device)
+    mp = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    _check(lib.ssa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, scale, mode, p0, p1, p2, n,
+                          _ptr(cnt), _ptr(mp), _stream(q)))
+    return o, lse, cnt, mp
 
 
 def fwd_debug(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,

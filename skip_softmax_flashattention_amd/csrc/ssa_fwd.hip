@@ -84,6 +84,7 @@ struct Params {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
+  float* maxp;                 // largest softmax weight of each row (nullable)
   int32_t* counts;
   uint8_t* mask;
   float* margin;
@@ -491,6 +492,16 @@ void ssa_fwd_kernel(const Params p) {
       else
         p.lse[((long long)b * p.H + h) * p.S + row] = lse;
     }
+    if (p.maxp != nullptr && hf == 0) {
+      // exp(m - LSE) = 1 / l with l taken relative to the row maximum m: the
+      // largest weight of the row over the kept keys (clamped to 1, which
+      // fp32 rounding of m and of the exponentials can overshoot slightly).
+      const float mp = fminf(__builtin_amdgcn_exp2f(m_run * kLog2e - mb_ref) * inv, 1.f);
+      if (p.cu_seqlens != nullptr)
+        p.maxp[(long long)h * T + tok0 + row] = mp;
+      else
+        p.maxp[((long long)b * p.H + h) * p.S + row] = mp;
+    }
   }
   const long long nqb_seq = (S_b + kBQ - 1) / kBQ;
   if (p.counts != nullptr && lane == 0 && (wave & 1) == 0 && qb < nqb_seq) {
@@ -597,7 +608,8 @@ int launch(const Params& p, dim3 grid, hipStream_t stream) {
   return SSA_OK;
 }
 
-int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
+int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, float* maxp, int B, int H, int S,
+              int D,
               float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* counts, uint8_t* mask,
               float* margin, void* stream, bool debug) {
   int st = check_tensors(q, k, v, o, lse, H, D, scale);
@@ -609,6 +621,7 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
     return fail(SSA_ERR_UNSUPPORTED, "sequence length %d too large", S);
   if (counts != nullptr && !aligned(counts, 4)) return fail(SSA_ERR_INVALID_ARG, "skip_counts must be 4-byte aligned");
   if (margin != nullptr && !aligned(margin, 4)) return fail(SSA_ERR_INVALID_ARG, "tile_margin must be 4-byte aligned");
+  if (maxp != nullptr && !aligned(maxp, 4)) return fail(SSA_ERR_INVALID_ARG, "max_prob must be 4-byte aligned");
   if (debug && mask == nullptr) return fail(SSA_ERR_INVALID_ARG, "tile_mask must not be NULL");
   Params p{};
   st = resolve(mode, p0, p1, p2, seqlen, &p.ln_lambda, &p.vote);
@@ -621,6 +634,7 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.v = static_cast<const uint16_t*>(v);
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
+  p.maxp = maxp;
   p.counts = counts;
   p.mask = mask;
   p.margin = margin;
@@ -646,28 +660,35 @@ extern "C" {
 
 int ssa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
             float scale, float factor, int seqlen, int32_t* skip_counts, void* stream) {
-  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, SSA_MODE_FACTOR, factor, 0.0, 0.0, seqlen, skip_counts,
+  return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, SSA_MODE_FACTOR, factor, 0.0, 0.0, seqlen, skip_counts,
                    nullptr, nullptr, stream, false);
 }
 
 int ssa_fwd_threshold(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
                       float scale, float threshold, int32_t* skip_counts, void* stream) {
-  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, SSA_MODE_THRESHOLD, threshold, 0.0, 0.0, S, skip_counts,
+  return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, SSA_MODE_THRESHOLD, threshold, 0.0, 0.0, S, skip_counts,
                    nullptr, nullptr, stream, false);
 }
 
 int ssa_fwd_calibrated(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
                        int D, float scale, float a, float b, float target_sparsity, int seqlen, int32_t* skip_counts,
                        void* stream) {
-  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, SSA_MODE_CALIBRATED, a, b, target_sparsity, seqlen,
+  return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, SSA_MODE_CALIBRATED, a, b, target_sparsity, seqlen,
                    skip_counts, nullptr, nullptr, stream, false);
 }
 
 int ssa_fwd_debug(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
                   float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* skip_counts,
                   uint8_t* tile_mask, float* tile_margin, void* stream) {
-  return fwd_fixed(q, k, v, o, lse, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, tile_mask,
+  return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, tile_mask,
                    tile_margin, stream, true);
+}
+
+int ssa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
+               float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* skip_counts,
+               float* max_prob, void* stream) {
+  return fwd_fixed(q, k, v, o, lse, max_prob, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, nullptr,
+                   nullptr, stream, false);
 }
 
 int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,

@@ -258,6 +258,11 @@ def pin_max_weight_is_inverse_l(orc):
             w = math.exp(max(s) - lse[i])
             assert 1.0 / len(kept) - 1e-12 <= w <= 1.0 + 1e-12, (lam, i, w)
             assert abs(w - 1.0 / sum(math.exp(x - max(s)) for x in s)) < 1e-12
+        mp = orc.max_prob_head(q, k, scale, r.skipped, r.lse, block_q=8, block_k=16).reshape(-1)
+        for i in range(96):
+            kept = [c for c in range(96) if not r.skipped[i // 8, c // 16]]
+            s = [scale * float(np.dot(q[i], k[c])) for c in kept]
+            assert abs(mp[i] - 1.0 / sum(math.exp(x - max(s)) for x in s)) < 1e-12
 
 
 def pin_planted_dominant_key(orc):

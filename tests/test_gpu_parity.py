@@ -228,3 +228,35 @@ def test_errors_on_gpu(ssa):
     with pytest.raises(ssa.SsaError) as e:
         ssa.fwd(x, x, x, factor=1.0)
     assert e.value.code == -2
+
+
+# ---- largest softmax weight per row (max_prob = exp(m - LSE) = 1 / l) -----------------
+@pytest.mark.parametrize("case", ["tiny", "grid", "planted"])
+def test_max_prob(ssa, case):
+    if case == "tiny":
+        w, kw = inputs.tiny(), dict(factor=4.0)
+    elif case == "grid":
+        w, kw = inputs.grid_small(31, (3, 10, 13), heads=2), dict(threshold=0.05)
+    else:
+        w, kw = inputs.grid_small(32, (2, 8, 9), heads=2, sink_frac=0.02), dict(threshold=1e-3)
+    print(f"[case] max_prob {case} shape={tuple(w.q.shape)} {kw}", flush=True)
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    o, lse, cnt, mp = ssa.fwd_max_prob(q, k, v, scale=w.scale, **kw)
+    od, ld, cd, mask, _ = ssa.fwd_debug(q, k, v, scale=w.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, od) and torch.equal(lse, ld) and torch.equal(cnt, cd), "max_prob entry changed the outputs"
+    mask_np, mp_np = mask.cpu().numpy().astype(bool), mp.cpu().numpy()
+    B, H, S, D = w.q.shape
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            qd, kd, vd = (oracle.from_bf16(t[b, h]) for t in (w.q, w.k, w.v))
+            forced = oracle.skip_head(qd, kd, vd, w.scale, None, forced_skip=mask_np[b, h])
+            ref = oracle.max_prob_head(qd, kd, w.scale, mask_np[b, h], forced.lse).reshape(-1)[:S]
+            got = mp_np[b, h]
+            rel = np.abs(got - ref) / ref
+            worst = max(worst, float(rel.max()))
+            n_kept = (~mask_np[b, h]).sum(axis=1).repeat(64)[:S] * 128
+            assert (got <= 1.0).all() and (got >= 1.0 / n_kept * (1 - 1e-3)).all()
+    print(f"[case] max_prob {case}: max relative error {worst:.2e}", flush=True)
+    assert worst <= 3e-3
