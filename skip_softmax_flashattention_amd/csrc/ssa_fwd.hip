@@ -7,22 +7,22 @@
 //
 // Work decomposition.  One workgroup = 8 waves = 256 query rows of one
 // (sequence, head); each wave owns 32 rows, and the two waves 2g, 2g+1 form
-// the 64-row vote group g of the skip test.  Key tiles of 128 keys stream
-// through LDS (K and V double buffered, shared by all eight waves), copied
-// from global memory straight into LDS by buffer loads with the
-// LDS-destination bit; keys past the end of the sequence lie outside the
-// buffer resource's range and arrive as zeros.
+// the 64-row vote group g of the skip test.  Workgroups are renumbered so
+// that each XCD works through whole heads, sharing K/V tiles in its L2.
+// Key tiles of 128 keys stream through LDS (K and V double buffered, shared
+// by all eight waves), copied from global memory straight into LDS by
+// buffer loads with the LDS-destination bit; keys past the end of the
+// sequence lie outside the buffer resource's range and arrive as zeros.
 //
-// Ping-pong schedule.  Two waves share each SIMD.  Waves 0-3 (group A) and
-// 4-7 (group B) run the same two-cluster program per tile, B one cluster
-// behind A, with a workgroup barrier between clusters:
-//   C1  scores S^T = K Q^T (MFMA) with the row maximum folded in, then this
-//       wave's half of the vote, published in LDS
-//   C2  the vote group's decision; kept tiles: exponentials (VALU) of each
-//       32-key block interleaved with the P.V MFMAs of the previous block
-// so while one wave of a SIMD runs its QK^T MFMAs the other runs the
-// softmax and P.V of the previous tile, and the two halves of a vote group
-// exchange their votes across the C1/C2 barrier.
+// Ping-pong schedule.  Two waves share each SIMD: waves 0-3 (group A) and
+// 4-7 (group B).  Each tile goes through two phases per wave, one per slot,
+// with a workgroup barrier ending every slot:
+//   MFMA phase     O^T += V^T P^T of the previous tile (if it was kept), then
+//                  the scores S^T = K Q^T of this tile
+//   softmax phase  row maximum, the vote group's skip decision, and for a
+//                  kept tile the online-softmax update with P in bf16
+// Group B runs one slot behind group A, so in every slot one wave of each
+// SIMD feeds the matrix cores while the other runs the softmax.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  S^T is
 // 4 key blocks of 32 x 32: a lane holds one query row and 16 keys per block,
@@ -70,6 +70,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 16.f;               // P <= 2^16 before a rescale is forced
 constexpr int kSpinLimit = 1 << 14;                 // polls of the partner's vote before giving up
 constexpr unsigned kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
+constexpr int kXcds = 8;                            // XCDs of an MI355X, each with its own L2
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -163,7 +164,22 @@ void ssa_fwd_kernel(const Params p) {
   __shared__ int vote_lds[kWaves];      // (tile << 1) | pass of the wave's half of the vote
   __shared__ float margin_lds[kWaves];  // debug: the wave's margin for the tile
 
-  const int qg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware work order.  The dispatcher hands workgroup L (linear id) to
+  // XCD L % 8, each XCD with its own L2.  Renumber so that XCD x runs one
+  // contiguous range of the (query group, head, sequence) list: the 32 CUs
+  // of an XCD then stream the same head's K/V tiles at the same time and
+  // share them in their L2, instead of two heads per XCD at half the reuse.
+  int qg, h, b;
+  {
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int n = gx * gy * (int)gridDim.z;
+    const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int per = n / kXcds, rem = n % kXcds, xcd = L % kXcds;
+    const int W = xcd * per + (xcd < rem ? xcd : rem) + L / kXcds;
+    qg = W % gx;
+    h = (W / gx) % gy;
+    b = W / (gx * gy);
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hf = lane >> 5;
   const bool group_b = wave >= 4;
@@ -643,6 +659,8 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.H = H;
   p.S = S;
   p.qgroups = (S + kRowsPerWG - 1) / kRowsPerWG;
+  if ((long long)p.qgroups * H * B >= (1LL << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "more than 2^31 workgroups (B x H x ceil(S / %d))", kRowsPerWG);
   p.tok_stride = kD;
   p.head_stride = (long long)S * kD;
   p.seq_stride = (long long)H * S * kD;
@@ -721,6 +739,8 @@ int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
   p.H = H;
   p.S = max_seqlen;
   p.qgroups = (max_seqlen + kRowsPerWG - 1) / kRowsPerWG;
+  if ((long long)p.qgroups * H * nseq >= (1LL << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "more than 2^31 workgroups (nseq x H x ceil(max_seqlen / %d))", kRowsPerWG);
   p.tok_stride = (long long)H * kD;
   p.head_stride = kD;
   p.seq_stride = 0;
