@@ -23,4 +23,5 @@ from .skip_attention import (  # noqa: F401
     skip_head,
     skipped_mass_head,
     max_prob_head,
+    virtual_tile_head,
 )

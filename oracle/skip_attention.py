@@ -383,3 +383,51 @@ def skip_attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlen
         masks.append(r.skipped[0])
         counts.append(r.skip_counts[0])
     return o, lse, masks, np.concatenate(counts, axis=1)
+
+
+# --------------------------------------------------------------------------
+# Virtual tiles for skipped tiles: "Triage: Skip, Skim, or Refine Attention
+# Tiles in Video Diffusion Transformers", section 6.1 "Skipping with Virtual
+# Tiles".  A skipped tile is replaced by one virtual key, the mean of its
+# keys, whose score carries the log of the number of keys it stands for, and
+# one virtual value, the mean of its values; the virtual keys join the same
+# softmax as the real keys of the kept tiles.  Reading taken here: the
+# clusters are the key tiles themselves, and the virtual keys do not enter
+# the running maximum of the skip test, so the skip mask is that of the
+# plain method and the virtual keys change only l, O and LSE.
+# --------------------------------------------------------------------------
+def virtual_tile_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                      skipped: np.ndarray, qblocks: Optional[Iterable[int]] = None,
+                      block_q: int = BLOCK_Q, block_k: int = BLOCK_K):
+    """Softmax attention of each query block over the keys of its kept tiles
+    plus one virtual key per skipped tile t: key mean(k over t), score
+    scale * q . mean(k over t) + ln(n_t), value mean(v over t), with n_t the
+    number of keys of t (fewer than block_k for a ragged last tile).
+
+    q, k, v: [S, D] float64; skipped: [nb, nKT] decisions of the listed
+    q-blocks (all by default).  Returns (o [nb, block_q, D], lse [nb, block_q]);
+    padding rows are NaN.
+    """
+    S, D = q.shape
+    nkt = -(-S // block_k)
+    qbs = np.arange(-(-S // block_q)) if qblocks is None else np.asarray(list(qblocks), dtype=np.int64)
+    counts = np.array([min(S, (t + 1) * block_k) - t * block_k for t in range(nkt)], dtype=np.float64)
+    kmean = np.stack([k[t * block_k:min(S, (t + 1) * block_k)].mean(axis=0) for t in range(nkt)])
+    vmean = np.stack([v[t * block_k:min(S, (t + 1) * block_k)].mean(axis=0) for t in range(nkt)])
+    key_tile = np.arange(S) // block_k
+    o = np.full((len(qbs), block_q, v.shape[1]), np.nan)
+    lse = np.full((len(qbs), block_q), np.nan)
+    for j, qb in enumerate(qbs):
+        r0, r1 = int(qb) * block_q, min(S, (int(qb) + 1) * block_q)
+        sk = np.asarray(skipped[j], dtype=bool)
+        kept = ~sk[key_tile]
+        s_real = float(scale) * (q[r0:r1] @ k[kept].T)
+        s_virt = float(scale) * (q[r0:r1] @ kmean[sk].T) + np.log(counts[sk])[None, :]
+        s = np.concatenate([s_real, s_virt], axis=1)
+        vals = np.concatenate([v[kept], vmean[sk]], axis=0)
+        mx = s.max(axis=1, keepdims=True)
+        p = np.exp(s - mx)
+        den = p.sum(axis=1)
+        o[j, : r1 - r0] = (p @ vals) / den[:, None]
+        lse[j, : r1 - r0] = mx[:, 0] + np.log(den)
+    return o, lse

@@ -413,4 +413,88 @@ def pin_varlen_uses_own_length(orc):
     del rng
 
 
+# ------------------------------------------------------- virtual tiles (Triage)
+# "Triage: Skip, Skim, or Refine Attention Tiles in Video Diffusion
+# Transformers", section 6.1 "Skipping with Virtual Tiles": a skipped tile is
+# represented by its mean key, with a log-count correction of its score, and
+# its mean value, inside the same softmax as the real keys.
+def _random_mask(seed, nqb, nkt, p=0.5):
+    m = np.random.default_rng(seed).random((nqb, nkt)) < p
+    m[:, 0] = False                      # the first tile is never skipped
+    return m
+
+
+def pin_virtual_tiles_no_skip_is_dense(orc):
+    """With no skipped tile there is no virtual key: dense attention."""
+    q, k, v = _rand(40, 150, 16), _rand(41, 150, 16), _rand(42, 150, 16)
+    o, lse = orc.virtual_tile_head(q, k, v, 0.4, np.zeros((-(-150 // 8), -(-150 // 16)), bool),
+                                   block_q=8, block_k=16)
+    od, lsed = orc.dense_head(q, k, v, 0.4)
+    assert np.abs(o.reshape(-1, 16)[:150] - od).max() < 1e-12
+    assert np.abs(lse.reshape(-1)[:150] - lsed).max() < 1e-12
+
+
+def pin_virtual_tiles_exact_for_constant_tiles(orc):
+    """When all keys of every tile are equal, the mean key with the log-count
+    correction stands for its tile exactly: n e^(q.k) = sum over the tile of
+    e^(q.k), and the mean value times that weight is the tile's value sum.  So
+    any mask gives dense attention.  The last tile is ragged (n < block_k)."""
+    S, D, bk = 150, 16, 16
+    rng = np.random.default_rng(43)
+    kt_keys = rng.standard_normal((-(-S // bk), D))
+    k = kt_keys[np.arange(S) // bk]
+    q, v = rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    mask = _random_mask(44, -(-S // 8), -(-S // bk), p=0.6)
+    assert mask[:, -1].any()
+    o, lse = orc.virtual_tile_head(q, k, v, 0.7, mask, block_q=8, block_k=bk)
+    od, lsed = orc.dense_head(q, k, v, 0.7)
+    assert np.abs(o.reshape(-1, D)[:S] - od).max() < 1e-12, np.abs(o.reshape(-1, D)[:S] - od).max()
+    assert np.abs(lse.reshape(-1)[:S] - lsed).max() < 1e-12
+
+
+def pin_virtual_tiles_bruteforce(orc):
+    """Pure-Python softmax over (real score, value) pairs of kept tiles and
+    (mean-key score + ln n_t, mean value) pairs of skipped tiles."""
+    S, D, bq, bk, scale = 40, 4, 8, 16, 0.9
+    rng = np.random.default_rng(45)
+    q, k, v = (rng.standard_normal((S, D)) for _ in range(3))
+    mask = _random_mask(46, -(-S // bq), -(-S // bk), p=0.5)
+    mask[1, 2] = True
+    o, lse = orc.virtual_tile_head(q, k, v, scale, mask, block_q=bq, block_k=bk)
+    for i in range(S):
+        qb = i // bq
+        items = []
+        for t in range(-(-S // bk)):
+            keys = list(range(t * bk, min(S, (t + 1) * bk)))
+            if not mask[qb, t]:
+                for c in keys:
+                    items.append((scale * sum(q[i, d] * k[c, d] for d in range(D)), [v[c, d] for d in range(D)]))
+            else:
+                n = len(keys)
+                km = [sum(k[c, d] for c in keys) / n for d in range(D)]
+                vm = [sum(v[c, d] for c in keys) / n for d in range(D)]
+                items.append((scale * sum(q[i, d] * km[d] for d in range(D)) + math.log(n), vm))
+        mx = max(s_ for s_, _ in items)
+        ws = [math.exp(s_ - mx) for s_, _ in items]
+        den = sum(ws)
+        for d in range(D):
+            ref = sum(w * val[d] for w, (_, val) in zip(ws, items)) / den
+            assert abs(o[qb, i % bq, d] - ref) < 1e-12
+        assert abs(lse[qb, i % bq] - (mx + math.log(den))) < 1e-12
+
+
+def pin_virtual_tiles_between_skip_and_dense(orc):
+    """n e^(mean of the scores) <= sum of e^(score) (Jensen), so adding the
+    virtual keys raises the log-normaliser of the skip-only pass but never
+    above that of dense attention: LSE_skip <= LSE_virtual <= LSE_dense."""
+    q, k, v = _peaky_head(47, 300, 16, gain=4.0)
+    mask = _random_mask(48, -(-300 // 8), -(-300 // 16), p=0.6)
+    o, lse = orc.virtual_tile_head(q, k, v, 0.5, mask, block_q=8, block_k=16)
+    _, lse_skip = orc.masked_dense_head(q, k, v, 0.5, mask, block_q=8, block_k=16)
+    _, lse_dense = orc.dense_head(q, k, v, 0.5)
+    lv = lse.reshape(-1)[:300]
+    assert (lv >= lse_skip - 1e-12).all() and (lv <= lse_dense + 1e-12).all()
+    assert (lv > lse_skip + 1e-9).mean() > 0.5      # the virtual keys do add weight
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -62,6 +62,20 @@ MUTANTS = [
     ("varlen uses the packed length",
      "r = skip_attention(qs, ks, vs, scale, ln_lambda_f32(lambdas[bi]),",
      "r = skip_attention(qs, ks, vs, scale, ln_lambda_f32(lambdas[0]),"),
+    ("virtual score without the log count",
+     "s_virt = float(scale) * (q[r0:r1] @ kmean[sk].T) + np.log(counts[sk])[None, :]",
+     "s_virt = float(scale) * (q[r0:r1] @ kmean[sk].T)"),
+    ("virtual value is the tile sum",
+     "vmean = np.stack([v[t * block_k:min(S, (t + 1) * block_k)].mean(axis=0)",
+     "vmean = np.stack([v[t * block_k:min(S, (t + 1) * block_k)].sum(axis=0)"),
+    ("virtual key is the tile maximum",
+     "kmean = np.stack([k[t * block_k:min(S, (t + 1) * block_k)].mean(axis=0)",
+     "kmean = np.stack([k[t * block_k:min(S, (t + 1) * block_k)].max(axis=0)"),
+    ("ragged tile counted as full",
+     "counts = np.array([min(S, (t + 1) * block_k) - t * block_k for t in range(nkt)], dtype=np.float64)",
+     "counts = np.array([block_k for t in range(nkt)], dtype=np.float64)"),
+    ("virtual keys double-count kept keys",
+     "kept = ~sk[key_tile]", "kept = np.ones(S, dtype=bool)"),
 ]
 
 
