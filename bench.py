@@ -10,8 +10,10 @@ the speedup is an in-session ratio.
 Printed (one JSON line): effective TFLOP/s of the skip step (dense-equivalent
 4 B H S^2 D per call over the call's time) as ``value``; executed TFLOP/s and
 MFMA utilisation against the bf16 dense peak; the dense call's numbers; the
-speedup; a roofline entry for the kernel; and the CPU oracle timed on a
-bounded sample as a baseline only.
+speedup; a roofline entry for the kernel; the virtual-tile variant
+(fwd_virtual) timed beside the plain skip call with both outputs' relative L1
+distance to dense attention; and the CPU oracle timed on a bounded sample as
+a baseline only.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15]
 """
@@ -220,6 +222,31 @@ def main():
     s5 = float(np.mean([a[2].elapsed_time(a[3]) for a in e5]))
     del q5, k5, v5
 
+    # Virtual tiles for the skipped tiles (fwd_virtual, tile-mean pre-pass
+    # included) at the same lambda, interleaved with the plain skip call; and
+    # each call's relative L1 distance to the dense output.
+    ws = torch.empty(ssa.virtual_workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        ssa.fwd_virtual(q, k, v, factor=factor, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    ev_v = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(5, args.steps // 4))]
+    for a in ev_v:
+        a[0].record(stream)
+        ov, _, _ = ssa.fwd_virtual(q, k, v, factor=factor, scale=w.scale, workspace=ws)
+        a[1].record(stream)
+        a[2].record(stream)
+        os_, _, _ = skip()
+        a[3].record(stream)
+    torch.cuda.synchronize()
+    t_virt = float(np.mean([a[0].elapsed_time(a[1]) for a in ev_v]))
+    t_skip2 = float(np.mean([a[2].elapsed_time(a[3]) for a in ev_v]))
+    od, _, _ = dense()
+    torch.cuda.synchronize()
+    den = od.float().abs().sum()
+    rel_skip = float((os_.float() - od.float()).abs().sum() / den)
+    rel_virt = float((ov.float() - od.float()).abs().sum() / den)
+    del ov, os_, od, ws
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -267,6 +294,9 @@ def main():
             "tflop_per_call": round(dense_flops / 1e12, 4),
         },
         "speedup_vs_dense": round(t_d / t_s, 4),
+        "virtual_tiles": {"ms_mean": round(t_virt, 4), "plain_skip_ms_mean": round(t_skip2, 4),
+                          "overhead": round(t_virt / t_skip2 - 1.0, 4),
+                          "rel_l1_to_dense": round(rel_virt, 5), "plain_skip_rel_l1_to_dense": round(rel_skip, 5)},
         "ulysses8_share": {"heads": 5, "dense_ms": round(d5, 4), "skip_ms": round(s5, 4),
                            "dense_mfma_util": round(dense_flops / 8 / (d5 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "speedup_vs_dense": round(d5 / s5, 4)},

@@ -50,6 +50,7 @@
 #ifndef SSA_H_
 #define SSA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -119,6 +120,28 @@ int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
 int ssa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int S, int D, float scale, int mode, double p0, double p1, double p2,
                int seqlen, int32_t* skip_counts, float* max_prob, void* stream);
+
+/* Skipped tiles replaced by virtual tiles ("Triage: Skip, Skim, or Refine
+ * Attention Tiles in Video Diffusion Transformers", section 6.1 "Skipping
+ * with Virtual Tiles").  Same skip test and mask as ssa_fwd (the virtual keys
+ * never enter the running maximum the test uses); then each tile t that a
+ * query block skipped joins that block's softmax as one key, the mean of
+ * the tile's keys with score scale * (q_i . mean k) + ln(n_t), carrying the
+ * mean of the tile's values; n_t is the tile's number of keys (128, fewer
+ * for a ragged last tile).  o and lse are those of that softmax;
+ * skip_counts as for ssa_fwd.  Any of the three controls (see ssa_mode;
+ * S_b = seqlen).
+ * workspace: device memory of at least ssa_fwd_virtual_workspace_bytes(B, H,
+ * S) bytes, 16-byte aligned, owned by the caller, overwritten (the tile
+ * means: mean keys bf16 [B, H, ceil(S/128), 2, D] as a hi + lo pair, mean
+ * values bf16 [B, H, ceil(S/128), D]).  Enqueues two kernels (tile means,
+ * then attention).  At most 2048 key tiles (S <= 262144), else
+ * SSA_ERR_UNSUPPORTED. */
+size_t ssa_fwd_virtual_workspace_bytes(int B, int H, int S);
+int ssa_fwd_virtual(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int S, int D, float scale, int mode, double p0, double p1,
+                    double p2, int seqlen, int32_t* skip_counts, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Any of the three controls (see ssa_mode; S_b = seqlen) with every tile
  * decision reported: tile_mask uint8 [B, H, ceil(S/64), ceil(S/128)]

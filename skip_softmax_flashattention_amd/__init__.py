@@ -24,7 +24,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "SsaError", "fwd", "fwd_varlen", "fwd_debug", "resolve_threshold", "device_check",
+    "SsaError", "fwd", "fwd_varlen", "fwd_debug", "fwd_max_prob", "fwd_virtual", "virtual_workspace_bytes",
+    "resolve_threshold", "device_check",
     "library_path", "load_library", "BLOCK_Q", "BLOCK_K", "HEAD_DIM",
     "MODE_FACTOR", "MODE_THRESHOLD", "MODE_CALIBRATED",
 ]
@@ -70,8 +71,13 @@ def load_library() -> ctypes.CDLL:
     lib.ssa_fwd_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, D, D, D, P, P]
     lib.ssa_fwd_debug.argtypes = [P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, P, P]
     lib.ssa_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, P]
+    Z = ctypes.c_size_t
+    lib.ssa_fwd_virtual.argtypes = [P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, Z, P]
+    lib.ssa_fwd_virtual_workspace_bytes.argtypes = [I, I, I]
+    lib.ssa_fwd_virtual_workspace_bytes.restype = Z
     lib.ssa_resolve_threshold.argtypes = [I, D, D, D, I, ctypes.POINTER(F), ctypes.POINTER(I)]
     for name in ("ssa_fwd", "ssa_fwd_threshold", "ssa_fwd_calibrated", "ssa_fwd_varlen", "ssa_fwd_debug", "ssa_fwd_ex",
+                 "ssa_fwd_virtual",
                  "ssa_resolve_threshold", "ssa_device_check", "ssa_version"):
         getattr(lib, name).restype = I
     lib.ssa_device_check.argtypes = []
@@ -200,6 +206,40 @@ def fwd_max_prob(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Op
     _check(lib.ssa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, scale, mode, p0, p1, p2, n,
                           _ptr(cnt), _ptr(mp), _stream(q)))
     return o, lse, cnt, mp
+
+
+def virtual_workspace_bytes(B: int, H: int, S: int) -> int:
+    """Bytes of device workspace fwd_virtual needs (the per-tile means)."""
+    return int(load_library().ssa_fwd_virtual_workspace_bytes(int(B), int(H), int(S)))
+
+
+def fwd_virtual(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+                factor: Optional[float] = None, threshold: Optional[float] = None, calib=None,
+                seqlen: Optional[int] = None, workspace: Optional[torch.Tensor] = None):
+    """fwd with every skipped tile replaced by a virtual key (the tile's mean
+    key, score + ln n_t) carrying the tile's mean value ("Triage: Skip, Skim,
+    or Refine Attention Tiles in Video Diffusion Transformers", section 6.1).
+    The skip mask and counts are those of fwd.  ``workspace`` (a device tensor
+    of at least virtual_workspace_bytes(B, H, S) bytes) is allocated when not
+    given.  Returns (o, lse, skip_counts)."""
+    _check_qkv(q, k, v, 4)
+    B, H, S, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    mode, p0, p1, p2 = _control(factor, threshold, calib)
+    n = S if seqlen is None else int(seqlen)
+    need = virtual_workspace_bytes(B, H, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    cnt = torch.empty((B, H, -(-S // BLOCK_Q)), dtype=torch.int32, device=q.device)
+    lib = load_library()
+    _check(lib.ssa_fwd_virtual(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, scale, mode, p0, p1, p2,
+                               n, _ptr(cnt), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(q)))
+    return o, lse, cnt
 
 
 def fwd_debug(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,

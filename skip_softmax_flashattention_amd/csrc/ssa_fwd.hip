@@ -37,6 +37,14 @@
 // m the true running maximum over the kept tiles.  A skipped tile costs only
 // its QK^T and row maximum; m, l and O are left untouched.
 //
+// Virtual tiles (the compensated entry).  Each vote group records its skip
+// decisions; after the last tile, every skipped tile t adds one virtual key,
+// the mean of its keys with score + ln(n_t), and the mean of its values to
+// the row's softmax ("Triage: Skip, Skim, or Refine Attention Tiles in Video
+// Diffusion Transformers", section 6.1).  The tile means come from a
+// pre-pass; the virtual scores and their P.V run on MFMA, 32 tiles at a time.
+// They never enter the running maximum the skip test uses.
+//
 // Exponent reference.  The exponentials use a per-row reference r <= m and
 // O, l are rescaled only when m climbs more than kRescaleLog2 binades above
 // r (then r = m).  This changes only rounding: O / l and r + ln(l) do not
@@ -71,6 +79,8 @@ constexpr float kRescaleLog2 = 16.f;               // P <= 2^16 before a rescale
 constexpr int kSpinLimit = 1 << 14;                 // polls of the partner's vote before giving up
 constexpr unsigned kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
 constexpr int kXcds = 8;                            // XCDs of an MI355X, each with its own L2
+constexpr int kCompWords = 64;                      // virtual tiles: 32 skip bits per word, up to 2048 tiles
+constexpr int kCompRound = 128;                     // virtual tiles staged in LDS per round
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -90,6 +100,8 @@ struct Params {
   uint8_t* mask;
   float* margin;
   const int32_t* cu_seqlens;   // null: fixed-length [B, H, S, D]
+  const uint16_t* kbar;        // virtual tiles: [B, H, nKT, 2, D] bf16 mean key (hi, lo)
+  const uint16_t* vbar;        // virtual tiles: [B, H, nKT, D] bf16 mean value
   int nseq;                    // B
   int H;
   int S;                       // fixed length, or max_seqlen
@@ -156,13 +168,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
 
-template <bool kDebug>
+template <bool kDebug, bool kComp>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssa_fwd_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
   __shared__ int vote_lds[kWaves];      // (tile << 1) | pass of the wave's half of the vote
   __shared__ float margin_lds[kWaves];  // debug: the wave's margin for the tile
+  __shared__ uint32_t comp_bits[kComp ? kWaves / 2 * kCompWords : 1];   // skip bits per vote group
 
   // XCD-aware work order.  The dispatcher hands workgroup L (linear id) to
   // XCD L % 8, each XCD with its own L2.  Renumber so that XCD x runs one
@@ -269,6 +282,7 @@ void ssa_fwd_kernel(const Params p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   int nskip = 0;
+  uint32_t comp_cur = 0;   // virtual tiles: skip bits of the current 32-tile word
 
   // Scores of the tile between its MFMA and softmax phases.  The softmax
   // phase of a kept tile overwrites them in place with P in bf16: register
@@ -392,6 +406,15 @@ void ssa_fwd_kernel(const Params p) {
         }
       }
     }
+    if constexpr (kComp) {
+      // The decision is uniform over the wave; the even wave of the group
+      // stores each completed word of 32 decisions.
+      if (skip) comp_cur |= 1u << (kt & 31);
+      if ((kt & 31) == 31 || kt == nkt - 1) {
+        if (lane == 0 && (wave & 1) == 0) comp_bits[(wave >> 1) * kCompWords + (kt >> 5)] = comp_cur;
+        comp_cur = 0;
+      }
+    }
     if (skip) {
       ++nskip;
       p_ready = false;
@@ -476,6 +499,95 @@ void ssa_fwd_kernel(const Params p) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
 
+  // ---- virtual tiles: add each skipped tile's mean key and value ----
+  if constexpr (kComp) {
+    const long long tbase = ((long long)b * p.H + h) * nkt;   // this head's first tile
+    const uint32_t* my_bits = comp_bits + (wave >> 1) * kCompWords;
+    for (int r0 = 0; r0 < nkt; r0 += kCompRound) {
+      // Stage kCompRound tiles in the free K/V buffers: for chunk c of 32
+      // tiles, mean-key hi rows at 64 c + t and lo rows at 64 c + 32 + t of
+      // lds_k (both buffers, 64 KB), mean values at row 32 c + t of lds_v[0]
+      // (the tile layouts the operand reads expect).  Tiles past the last one
+      // are zero.
+      __syncthreads();
+      constexpr int kKItems = kCompRound * 2 * 16, kItems = kCompRound * 3 * 16;
+#pragma unroll
+      for (int it = 0; it < kItems / kThreads; ++it) {
+        const int i = tid + kThreads * it;
+        const bool isk = i < kKItems;
+        const int ii = isk ? i : i - kKItems;
+        const int tr = isk ? ii >> 5 : ii >> 4;          // tile within the round
+        const int sel = isk ? (ii >> 4) & 1 : 0;          // 0: hi, 1: lo
+        const int j = ii & 15;                            // 16-byte chunk of the row
+        const int t = r0 + tr;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (t < nkt) {
+          const uint16_t* src = isk ? p.kbar + ((tbase + t) * 2 + sel) * kD : p.vbar + (tbase + t) * kD;
+          val = *reinterpret_cast<const u32x4*>(src + 8 * j);
+        }
+        const int row = isk ? 64 * (tr >> 5) + 32 * sel + (tr & 31) : tr;
+        unsigned char* dst = (isk ? &lds_k[0][0] : lds_v[0]) + row * kRowBytes + 16 * (j ^ swz(row));
+        *reinterpret_cast<u32x4*>(dst) = val;
+      }
+      __syncthreads();
+      for (int c = 0; c < kCompRound / 32 && r0 + 32 * c < nkt; ++c) {
+        const int ch = (r0 >> 5) + c;                     // 32-tile word of the skip bits
+        const uint32_t bits = my_bits[ch];
+        if (bits == 0) continue;                          // this vote group skipped none of them
+        const unsigned char* kc = &lds_k[0][0] + 64 * c * kRowBytes;
+        const unsigned char* vc = lds_v[0] + 32 * c * kRowBytes;
+        // Virtual scores S^T = Kbar Q^T of the 32 tiles (hi and lo parts).
+        f32x16 shi = f32x16{}, slo = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int off = krow * kRowBytes + 16 * ((2 * s + hf) ^ kswz);
+          const bf16x8 ahi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kc + off));
+          const bf16x8 alo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kc + 32 * kRowBytes + off));
+          shi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qf[s], shi, 0, 0, 0);
+          slo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qf[s], slo, 0, 0, 0);
+        }
+        // Weights n_t exp(scale s - r) of this group's skipped tiles, in bf16
+        // pairs laid out as the P^T operand; register r holds tile
+        // 16 (r / 8) + 8 hf + r % 8 of the chunk.
+        uint32_t pw[8];
+        float ws = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float e[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int tl = 16 * ((r + u) >> 3) + 8 * hf + ((r + u) & 7);
+            const int t = 32 * ch + tl;
+            e[u] = 0.f;
+            if (((bits >> tl) & 1u) != 0 && t < nkt) {
+              const int n_t = min(kBK, S_b - kBK * t);
+              e[u] = __builtin_amdgcn_exp2f(
+                  fmaf(shi[r + u] + slo[r + u], p.scale_log2e, __builtin_amdgcn_logf((float)n_t) - mb_ref));
+            }
+            ws += e[u];
+          }
+          pw[r >> 1] = pack_bf16(e[0], e[1]);
+        }
+        l += ws;
+        // O^T += Vbar^T P^T over the 32 tiles (two 16-tile steps).
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 pb = {pw[4 * t2], pw[4 * t2 + 1], pw[4 * t2 + 2], pw[4 * t2 + 3]};
+          const unsigned char* vstep = vc + 16 * t2 * kRowBytes;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                               __builtin_bit_cast(bf16x8, pb), oacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
   // ---- epilogue: O / l in bf16, LSE = r + ln l, skipped-tile count ----
   long long T = 0, qb_total = 0, qb_off = 0;
   if (p.cu_seqlens != nullptr) {
@@ -530,6 +642,60 @@ void ssa_fwd_kernel(const Params p) {
   }
 }
 
+// Mean key and mean value of every key tile of a fixed-length [B, H, S, D]
+// problem, for the virtual tiles: one workgroup of 256 threads per tile.
+// Thread t sums channels 8 (t % 16) .. + 7 over the keys t / 16, t / 16 + 16,
+// ... of the tile (16-byte loads, 256 contiguous bytes per key row), in fp32;
+// the 16 partial sums of each channel are then added in LDS in a fixed
+// order.  The mean key is stored as a bf16 pair hi + lo (hi = bf16(mean),
+// lo = bf16(mean - hi)), the mean value as bf16.
+__global__ __launch_bounds__(256) void tile_means_kernel(const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           uint16_t* __restrict__ kbar,
+                                                           uint16_t* __restrict__ vbar, int H, int S) {
+  __shared__ float part[2][16][kD];
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nkt = (S + kBK - 1) / kBK;
+  const int g = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const long long row0 = ((long long)b * H + h) * S + (long long)t * kBK;
+  const int n = min(kBK, S - kBK * t);
+#pragma unroll
+  for (int isv = 0; isv < 2; ++isv) {
+    const uint16_t* src = (isv ? v : k) + row0 * kD + 8 * g;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kBK / 16; ++i) {
+      const int key = r + 16 * i;
+      if (key < n) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src + (long long)key * kD);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(x[e] << 16);
+          acc[2 * e + 1] += __uint_as_float(x[e] & 0xffff0000u);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[isv][r][8 * g + e] = acc[e];
+  }
+  __syncthreads();
+  const int c = threadIdx.x & (kD - 1);
+  const int isv = threadIdx.x >> 7;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += part[isv][i][c];
+  const float mean = sum / (float)n;
+  const long long tile = ((long long)b * H + h) * nkt + t;
+  const uint32_t hi = pack_bf16(mean, 0.f) & 0xffffu;
+  if (isv) {
+    vbar[tile * kD + c] = (uint16_t)hi;
+  } else {
+    const float lo = mean - __uint_as_float(hi << 16);
+    kbar[(tile * 2) * kD + c] = (uint16_t)hi;
+    kbar[(tile * 2 + 1) * kD + c] = (uint16_t)(pack_bf16(lo, 0.f) & 0xffffu);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
@@ -570,6 +736,14 @@ int check_device() {
 }
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+// Bytes of the virtual-tile workspace: mean keys [B, H, nKT, 2, D] and mean
+// values [B, H, nKT, D], bf16.
+size_t comp_workspace_bytes(int B, int H, int S) {
+  if (B <= 0 || H <= 0 || S <= 0) return 0;
+  const size_t nkt = (size_t)((S + kBK - 1) / kBK);
+  return (size_t)B * H * nkt * 3 * kD * sizeof(uint16_t);
+}
 
 int check_tensors(const void* q, const void* k, const void* v, const void* o, const float* lse, int H, int D, float scale) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
@@ -616,9 +790,9 @@ int resolve(int mode, double p0, double p1, double p2, int seqlen, float* ln_lam
   return SSA_OK;
 }
 
-template <bool kDebug>
+template <bool kDebug, bool kComp = false>
 int launch(const Params& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL(ssa_fwd_kernel<kDebug>, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((ssa_fwd_kernel<kDebug, kComp>), grid, dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SSA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SSA_OK;
@@ -627,7 +801,7 @@ int launch(const Params& p, dim3 grid, hipStream_t stream) {
 int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, float* maxp, int B, int H, int S,
               int D,
               float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* counts, uint8_t* mask,
-              float* margin, void* stream, bool debug) {
+              float* margin, void* stream, bool debug, void* comp_ws = nullptr, size_t comp_ws_bytes = 0) {
   int st = check_tensors(q, k, v, o, lse, H, D, scale);
   if (st != SSA_OK) return st;
   if (B < 0 || S < 0) return fail(SSA_ERR_INVALID_ARG, "negative batch or sequence length");
@@ -639,6 +813,16 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (margin != nullptr && !aligned(margin, 4)) return fail(SSA_ERR_INVALID_ARG, "tile_margin must be 4-byte aligned");
   if (maxp != nullptr && !aligned(maxp, 4)) return fail(SSA_ERR_INVALID_ARG, "max_prob must be 4-byte aligned");
   if (debug && mask == nullptr) return fail(SSA_ERR_INVALID_ARG, "tile_mask must not be NULL");
+  const bool comp = comp_ws != nullptr;
+  if (comp) {
+    if (!aligned(comp_ws, 16)) return fail(SSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (comp_ws_bytes < comp_workspace_bytes(B, H, S))
+      return fail(SSA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed", comp_ws_bytes,
+                  comp_workspace_bytes(B, H, S));
+    if ((S + kBK - 1) / kBK > 32 * kCompWords)
+      return fail(SSA_ERR_UNSUPPORTED, "virtual tiles support at most %d key tiles (S <= %d)", 32 * kCompWords,
+                  32 * kCompWords * kBK);
+  }
   Params p{};
   st = resolve(mode, p0, p1, p2, seqlen, &p.ln_lambda, &p.vote);
   if (st != SSA_OK) return st;
@@ -668,6 +852,18 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
   p.lambda_per_seq = 0;
   const dim3 grid(p.qgroups, H, B);
+  if (comp) {
+    const int nkt = (S + kBK - 1) / kBK;
+    uint16_t* kbar = static_cast<uint16_t*>(comp_ws);
+    uint16_t* vbar = kbar + (size_t)B * H * nkt * 2 * kD;
+    hipLaunchKernelGGL(tile_means_kernel, dim3(nkt, H, B), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       p.k, p.v, kbar, vbar, H, S);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSA_ERR_LAUNCH, "tile-mean launch failed: %s", hipGetErrorString(e));
+    p.kbar = kbar;
+    p.vbar = vbar;
+    return launch<false, true>(p, grid, static_cast<hipStream_t>(stream));
+  }
   return debug ? launch<true>(p, grid, static_cast<hipStream_t>(stream))
                : launch<false>(p, grid, static_cast<hipStream_t>(stream));
 }
@@ -707,6 +903,16 @@ int ssa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                float* max_prob, void* stream) {
   return fwd_fixed(q, k, v, o, lse, max_prob, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, nullptr,
                    nullptr, stream, false);
+}
+
+size_t ssa_fwd_virtual_workspace_bytes(int B, int H, int S) { return comp_workspace_bytes(B, H, S); }
+
+int ssa_fwd_virtual(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
+                    float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* skip_counts,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return fail(SSA_ERR_INVALID_ARG, "workspace must not be NULL");
+  return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, nullptr,
+                   nullptr, stream, false, workspace, workspace_bytes);
 }
 
 int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,

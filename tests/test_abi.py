@@ -21,7 +21,7 @@ FAKE = 1 << 20        # aligned non-null pointer value: validation never derefer
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(ssa_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ssa_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -121,3 +121,24 @@ def test_binding_rejects_two_controls():
         ssa.fwd(x, x, x)
     with pytest.raises(ValueError):   # CPU tensors are rejected, never computed on the host
         ssa.fwd(x, x, x, threshold=0.1)
+
+
+def test_virtual_workspace_size(lib):
+    """Mean keys (hi, lo) and mean values in bf16: 3 x 128 x 2 bytes per key tile."""
+    assert ssa.virtual_workspace_bytes(1, 40, 32760) == 40 * 256 * 3 * 128 * 2
+    assert ssa.virtual_workspace_bytes(2, 3, 129) == 2 * 3 * 2 * 768
+    assert ssa.virtual_workspace_bytes(0, 3, 129) == 0
+
+
+def test_virtual_argument_errors(lib):
+    need = ssa.virtual_workspace_bytes(1, 2, 256)
+
+    def call(ws=FAKE, ws_bytes=need, S=256, mode=0, p0=1.0):
+        return lib.ssa_fwd_virtual(FAKE, FAKE, FAKE, FAKE, None, 1, 2, S, 128, 0.088, mode, p0, 0.0, 0.0, S,
+                                   None, ws, ws_bytes, None)
+    assert call(ws=None) == INVALID
+    assert call(ws=FAKE + 8) == INVALID                    # misaligned workspace
+    assert call(ws_bytes=need - 1) == INVALID               # too small
+    assert "smaller" in lib.ssa_last_error().decode()
+    assert call(S=2048 * 128 + 1, ws_bytes=1 << 40) == UNSUPPORTED   # more than 2048 key tiles
+    assert call(p0=-1.0) == BAD_THRESHOLD
