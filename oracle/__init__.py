@@ -5,6 +5,7 @@ baseline may use this package; the library and its Python binding never do.
 It is plain numpy in float64 (the skip vote in float32, the kernel's
 precision) and shares no code with the HIP path.
 """
+from . import fp8  # noqa: F401
 from .skip_attention import (  # noqa: F401
     BLOCK_K,
     BLOCK_Q,
