@@ -12,8 +12,9 @@ Printed (one JSON line): effective TFLOP/s of the skip step (dense-equivalent
 MFMA utilisation against the bf16 dense peak; the dense call's numbers; the
 speedup; a roofline entry for the kernel; the virtual-tile variant
 (fwd_virtual) timed beside the plain skip call with both outputs' relative L1
-distance to dense attention; and the CPU oracle timed on a bounded sample as
-a baseline only.
+distance to dense attention; the FP8-score variant (quantize_qk_fp8 +
+fwd_fp8) at lambda = 0 and at the timed lambda; and the CPU oracle timed on a
+bounded sample as a baseline only.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15]
 """
@@ -247,6 +248,33 @@ def main():
     rel_virt = float((ov.float() - od.float()).abs().sum() / den)
     del ov, os_, od, ws
 
+    # FP8 scores (quantize_qk_fp8 + fwd_fp8): the quantisation pass, then the
+    # FP8-score kernel at lambda = 0 and at the timed lambda, interleaved with
+    # the bf16 dense call; the FP8 call's own skip fraction at that lambda.
+    q8, k8, qs8, ks8 = ssa.quantize_qk_fp8(q, k)
+    _, _, c8 = ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=factor, scale=w.scale)
+    ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=0.0, scale=w.scale)
+    torch.cuda.synchronize()
+    n8 = max(5, args.steps // 4)
+    ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(n8)]
+    for a in ev8:
+        a[0].record(stream)
+        ssa.quantize_qk_fp8(q, k)
+        a[1].record(stream)
+        a[2].record(stream)
+        ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=0.0, scale=w.scale)
+        a[3].record(stream)
+        a[4].record(stream)
+        ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=factor, scale=w.scale)
+        a[5].record(stream)
+        a[6].record(stream)
+        dense()
+        a[7].record(stream)
+    torch.cuda.synchronize()
+    t8 = [float(np.mean([a[2 * i].elapsed_time(a[2 * i + 1]) for a in ev8])) for i in range(4)]
+    fp8_skip_frac = float(c8.sum()) / float(mask_np.size)
+    del q8, k8, qs8, ks8, c8
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -297,6 +325,11 @@ def main():
         "virtual_tiles": {"ms_mean": round(t_virt, 4), "plain_skip_ms_mean": round(t_skip2, 4),
                           "overhead": round(t_virt / t_skip2 - 1.0, 4),
                           "rel_l1_to_dense": round(rel_virt, 5), "plain_skip_rel_l1_to_dense": round(rel_skip, 5)},
+        "fp8_scores": {"quantize_ms": round(t8[0], 4), "dense_ms": round(t8[1], 4), "skip_ms": round(t8[2], 4),
+                       "bf16_dense_ms": round(t8[3], 4), "skip_fraction": round(fp8_skip_frac, 4),
+                       "dense_effective_tflops": round(dense_flops / (t8[1] * 1e-3) / 1e12, 2),
+                       "skip_effective_tflops_incl_quantize": round(dense_flops / ((t8[0] + t8[2]) * 1e-3) / 1e12, 2),
+                       "skip_speedup_vs_bf16_dense_incl_quantize": round(t8[3] / (t8[0] + t8[2]), 4)},
         "ulysses8_share": {"heads": 5, "dense_ms": round(d5, 4), "skip_ms": round(s5, 4),
                            "dense_mfma_util": round(dense_flops / 8 / (d5 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "speedup_vs_dense": round(d5 / s5, 4)},

@@ -143,6 +143,34 @@ int ssa_fwd_virtual(const void* q, const void* k, const void* v, void* o, float*
                     double p2, int seqlen, int32_t* skip_counts, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* FP8 scores.  The score matmul Q K^T runs on 8-bit floating point at the
+ * doubled matrix rate while P.V keeps bf16 inputs (video-attention blog post
+ * on Wan 2.2, sections "First, the hardware ceiling" and "Where the 1.33x
+ * ceiling comes from, exactly": only the score half moves to the low
+ * precision).  Format: OCP FP8 E4M3 (bias 7, largest finite value 448).
+ *
+ * ssa_quantize_qk_fp8: q, k bf16 [B, H, S, D] (16-byte aligned) to E4M3 codes
+ * q8, k8 uint8 [B, H, S, D] (8-byte aligned) with q_scale float [B, H, S]
+ * (one per token) and k_scale float [B, H, ceil(S/128)] (one per tile of 128
+ * keys).  A block's scale is its largest magnitude / 448 (float32 division;
+ * 1 for an all-zero block); each value is divided by its scale (float32),
+ * clamped to +-448 and rounded to the nearest code, ties to even.  Enqueues
+ * two kernels.
+ *
+ * ssa_fwd_fp8: the method of ssa_fwd with scores
+ * s_ic = scale * q_scale_i * k_scale_t(c) * (decode(q8_i) . decode(k8_c)),
+ * summed by the E4M3 MFMA in fp32; v, o bf16 [B, H, S, D] as in ssa_fwd;
+ * the skip test, threshold controls (ssa_mode), lse and skip_counts as in
+ * ssa_fwd_ex.  tile_mask and tile_margin (nullable; tile_margin needs
+ * tile_mask) report the decisions as ssa_fwd_debug does.  At most 4096 key
+ * tiles (S <= 524288), else SSA_ERR_UNSUPPORTED. */
+int ssa_quantize_qk_fp8(const void* q, const void* k, uint8_t* q8, uint8_t* k8, float* q_scale,
+                        float* k_scale, int B, int H, int S, int D, void* stream);
+int ssa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const float* q_scale, const float* k_scale,
+                const void* v, void* o, float* lse, int B, int H, int S, int D, float scale, int mode,
+                double p0, double p1, double p2, int seqlen, int32_t* skip_counts,
+                uint8_t* tile_mask, float* tile_margin, void* stream);
+
 /* Any of the three controls (see ssa_mode; S_b = seqlen) with every tile
  * decision reported: tile_mask uint8 [B, H, ceil(S/64), ceil(S/128)]
  * (1 = skipped) and tile_margin float (same shape, nullable): the largest

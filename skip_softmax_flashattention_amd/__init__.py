@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "SsaError", "fwd", "fwd_varlen", "fwd_debug", "fwd_max_prob", "fwd_virtual", "virtual_workspace_bytes",
-    "resolve_threshold", "device_check",
+    "quantize_qk_fp8", "fwd_fp8", "resolve_threshold", "device_check",
     "library_path", "load_library", "BLOCK_Q", "BLOCK_K", "HEAD_DIM",
     "MODE_FACTOR", "MODE_THRESHOLD", "MODE_CALIBRATED",
 ]
@@ -75,9 +75,11 @@ def load_library() -> ctypes.CDLL:
     lib.ssa_fwd_virtual.argtypes = [P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, Z, P]
     lib.ssa_fwd_virtual_workspace_bytes.argtypes = [I, I, I]
     lib.ssa_fwd_virtual_workspace_bytes.restype = Z
+    lib.ssa_quantize_qk_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+    lib.ssa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, D, D, D, I, P, P, P, P]
     lib.ssa_resolve_threshold.argtypes = [I, D, D, D, I, ctypes.POINTER(F), ctypes.POINTER(I)]
     for name in ("ssa_fwd", "ssa_fwd_threshold", "ssa_fwd_calibrated", "ssa_fwd_varlen", "ssa_fwd_debug", "ssa_fwd_ex",
-                 "ssa_fwd_virtual",
+                 "ssa_fwd_virtual", "ssa_quantize_qk_fp8", "ssa_fwd_fp8",
                  "ssa_resolve_threshold", "ssa_device_check", "ssa_version"):
         getattr(lib, name).restype = I
     lib.ssa_device_check.argtypes = []
@@ -240,6 +242,50 @@ def fwd_virtual(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Opt
                                n, _ptr(cnt), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(q)))
     return o, lse, cnt
+
+
+def quantize_qk_fp8(q: torch.Tensor, k: torch.Tensor):
+    """OCP E4M3 codes of q and k with their scales: returns (q8 uint8 [B, H, S,
+    128], k8 uint8 [B, H, S, 128], q_scale float32 [B, H, S] (per token),
+    k_scale float32 [B, H, ceil(S/128)] (per 128-key tile))."""
+    _check_qkv(q, k, k, 4)
+    B, H, S, D = q.shape
+    q8 = torch.empty((B, H, S, D), dtype=torch.uint8, device=q.device)
+    k8 = torch.empty((B, H, S, D), dtype=torch.uint8, device=q.device)
+    qs = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    ks = torch.empty((B, H, -(-S // BLOCK_K)), dtype=torch.float32, device=q.device)
+    _check(load_library().ssa_quantize_qk_fp8(_ptr(q), _ptr(k), _ptr(q8), _ptr(k8), _ptr(qs), _ptr(ks), B, H, S, D,
+                                              _stream(q)))
+    return q8, k8, qs, ks
+
+
+def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_scale: torch.Tensor, k_scale: torch.Tensor, v: torch.Tensor, *,
+            scale: Optional[float] = None, factor: Optional[float] = None, threshold: Optional[float] = None,
+            calib=None, seqlen: Optional[int] = None, debug: bool = False):
+    """Skip-softmax attention with FP8 scores (operands from quantize_qk_fp8)
+    and bf16 P.V.  Returns (o, lse, skip_counts), plus (tile_mask, tile_margin)
+    when ``debug``."""
+    if v.dtype != torch.bfloat16 or v.dim() != 4 or not v.is_contiguous() or v.device.type != "cuda":
+        raise ValueError("v must be a contiguous bf16 [B, H, S, 128] CUDA (HIP) tensor")
+    B, H, S, D = v.shape
+    for name, t, dt, shape in (("q8", q8, torch.uint8, (B, H, S, D)), ("k8", k8, torch.uint8, (B, H, S, D)),
+                               ("q_scale", q_scale, torch.float32, (B, H, S)),
+                               ("k_scale", k_scale, torch.float32, (B, H, -(-S // BLOCK_K)))):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != v.device:
+            raise ValueError(f"{name} must be a contiguous {dt} {shape} tensor on the device of v")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    mode, p0, p1, p2 = _control(factor, threshold, calib)
+    n = S if seqlen is None else int(seqlen)
+    nqb, nkt = -(-S // BLOCK_Q), -(-S // BLOCK_K)
+    o = torch.empty_like(v)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=v.device)
+    cnt = torch.empty((B, H, nqb), dtype=torch.int32, device=v.device)
+    mask = torch.empty((B, H, nqb, nkt), dtype=torch.uint8, device=v.device) if debug else None
+    margin = torch.empty((B, H, nqb, nkt), dtype=torch.float32, device=v.device) if debug else None
+    _check(load_library().ssa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(q_scale), _ptr(k_scale), _ptr(v), _ptr(o), _ptr(lse),
+                                      B, H, S, D, scale, mode, p0, p1, p2, n, _ptr(cnt), _ptr(mask), _ptr(margin),
+                                      _stream(v)))
+    return (o, lse, cnt, mask, margin) if debug else (o, lse, cnt)
 
 
 def fwd_debug(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,

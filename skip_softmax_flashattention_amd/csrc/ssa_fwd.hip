@@ -81,12 +81,16 @@ constexpr unsigned kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data fo
 constexpr int kXcds = 8;                            // XCDs of an MI355X, each with its own L2
 constexpr int kCompWords = 64;                      // virtual tiles: 32 skip bits per word, up to 2048 tiles
 constexpr int kCompRound = 128;                     // virtual tiles staged in LDS per round
+constexpr int kRow8 = kD;                           // one FP8 row of 128 channels (bytes)
+constexpr int kTile8Bytes = kBK * kRow8;            // 16 KB
+constexpr int kMaxTilesFp8 = 4096;                  // FP8 scores: K tile scales staged in LDS
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 struct Params {
@@ -102,6 +106,10 @@ struct Params {
   const int32_t* cu_seqlens;   // null: fixed-length [B, H, S, D]
   const uint16_t* kbar;        // virtual tiles: [B, H, nKT, 2, D] bf16 mean key (hi, lo)
   const uint16_t* vbar;        // virtual tiles: [B, H, nKT, D] bf16 mean value
+  const uint8_t* q8;           // FP8 scores: E4M3 codes [B, H, S, D] of q and k
+  const uint8_t* k8;
+  const float* q_scale;        // FP8 scores: [B, H, S] per-token scale of q
+  const float* k_scale;        // FP8 scores: [B, H, nKT] per-tile scale of k
   int nseq;                    // B
   int H;
   int S;                       // fixed length, or max_seqlen
@@ -168,14 +176,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
 
-template <bool kDebug, bool kComp>
+template <bool kDebug, bool kComp, bool kFp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssa_fwd_kernel(const Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kFp8 ? kTile8Bytes : kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
   __shared__ int vote_lds[kWaves];      // (tile << 1) | pass of the wave's half of the vote
   __shared__ float margin_lds[kWaves];  // debug: the wave's margin for the tile
   __shared__ uint32_t comp_bits[kComp ? kWaves / 2 * kCompWords : 1];   // skip bits per vote group
+  __shared__ float kscale_lds[kFp8 ? kMaxTilesFp8 : 1];                 // FP8 scores: scale of each K tile
 
   // XCD-aware work order.  The dispatcher hands workgroup L (linear id) to
   // XCD L % 8, each XCD with its own L2.  Renumber so that XCD x runs one
@@ -226,7 +235,29 @@ void ssa_fwd_kernel(const Params p) {
   // Q^T operand fragments: qf[s] = Q[wrow0 + c][16 s + 8 hf .. +7] (rows past
   // the end read as zeros).
   bf16x8 qf[8];
-  {
+  // FP8 scores: Q^T operand of the 32 x 32 x 64 MFMA, qf8[s] = codes
+  // Q8[wrow0 + c][64 s + 32 hf .. +31]; K tiles are E4M3 codes as well, and
+  // the scores are scale * q_scale[row] * k_scale[tile] * (Q8 . K8).
+  i32x8 qf8[2];
+  float sq_row = 0.f;                     // scale * q_scale of this lane's row
+  const long long head8 = ((long long)b * p.H + h) * p.S;   // first token of this head (FP8 arrays)
+  __amdgpu_buffer_rsrc_t rk8 = rk;
+  if constexpr (kFp8) {
+    const uint32_t range8 = (uint32_t)S_b * kRow8;
+    const __amdgpu_buffer_rsrc_t rq8 = make_rsrc(p.q8 + head8 * kRow8, range8);
+    rk8 = make_rsrc(p.k8 + head8 * kRow8, range8);
+    const uint32_t off = (uint32_t)(wrow0 + c) * kRow8 + 32u * hf;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq8, off + 64u * s, 0, 0));
+      const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq8, off + 64u * s + 16u, 0, 0));
+      qf8[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    // padding rows take any positive factor: they neither vote nor are stored
+    sq_row = valid ? p.scale * p.q_scale[head8 + wrow0 + c] : p.scale;
+    // the head's K tile scales, read by every softmax phase
+    for (int t = tid; t < nkt; t += kThreads) kscale_lds[t] = p.k_scale[((long long)b * p.H + h) * nkt + t];
+  } else {
     const uint32_t off = (uint32_t)(wrow0 + c) * ts_bytes + 16u * hf;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
@@ -254,10 +285,34 @@ void ssa_fwd_kernel(const Params p) {
                                                copy_off[j] + goff, 0, 0, 0);
   };
 
+  // FP8 K tile copy: 128-byte rows, 8 rows (1 KB) per instruction; lane l
+  // lands at row + l / 8, physical chunk l % 8, which holds logical chunk
+  // (l % 8) ^ swz8(row) with swz8(row) = (row / 2) % 8 (equal for rows 16
+  // apart).
+  uint32_t copy_off8[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    copy_off8[j] = (uint32_t)r * kRow8 + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
+  }
+  // The 16-row block `blk` (0..7) of FP8 K tile kt into the LDS tile at dst.
+  auto copy_block8 = [&](int kt, unsigned char* dst, int blk) __attribute__((always_inline)) {
+    const uint32_t goff = (uint32_t)(kt * kBK + 16 * blk) * kRow8;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk8, LDS_PTR(void, dst + (16 * blk + 8 * j) * kRow8), 16,
+                                               copy_off8[j] + goff, 0, 0, 0);
+  };
+  auto copy_k = [&](int kt, unsigned char* dst, int blk) __attribute__((always_inline)) {
+    if constexpr (kFp8) copy_block8(kt, dst, blk);
+    else copy_block(rk, kt, dst, blk);
+  };
+
   // Per-lane LDS byte offsets of the operand reads.
   // K operand (A of S^T): row 32 kb + key_perm(c), logical chunk 2 s + hf.
   const int krow = key_perm(c);
   const int kswz = swz(krow);
+  const int kswz8 = (krow >> 1) & 7;     // FP8 K rows: swz8 of row 32 kb + krow
   // V^T operand (A of O^T) via transpose reads: within 16-lane group g the
   // lane 4 e + q supplies row 8 hf + 4 ih + e (plus the 16-key step base),
   // channels 32 db + 16 (g % 2) + 4 q .. +3.
@@ -347,6 +402,81 @@ void ssa_fwd_kernel(const Params p) {
     }
   };
 
+  // ---- FP8-score MFMA phase: O^T += V^T P^T for the previous tile (bf16,
+  // as above), then S^T = K8 Q8^T for tile kt with 8 MFMAs of 32 x 32 x 64
+  // (E4M3 x E4M3, fp32 accumulate).  One ring of 8 slots of 16 bytes feeds
+  // both: a V^T fragment takes one slot (two transpose reads), a K fragment
+  // two (two 16-byte reads); slots are refilled 8 loads ahead.
+  auto mfma_phase8 = [&](auto pv_c, auto qk_c, int kt) __attribute__((always_inline)) {
+    constexpr bool kPV = decltype(pv_c)::value, kQK = decltype(qk_c)::value;
+    constexpr int L0 = kPV ? 0 : 32, L1 = kQK ? 48 : 32;   // loads [L0, L1): < 32 V^T, >= 32 K halves
+    const unsigned char* vl = lds_v[(kt - 1) & 1];
+    const unsigned char* kl = lds_k[kt & 1];
+    auto load = [&](int L) __attribute__((always_inline)) {
+      if (L < 32) {
+        const int kb = L >> 3, t2 = (L >> 2) & 1, db = L & 3;
+        const unsigned char* vstep = vl + (32 * kb + 16 * t2) * kRowBytes;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[0][db]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vstep + voff[1][db]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+      }
+      const int j = (L - 32) >> 1, hh = (L - 32) & 1;
+      const int s = j >> 2, kb = j & 3;
+      const int off = (32 * kb + krow) * kRow8 + 16 * ((4 * s + 2 * hf + hh) ^ kswz8);
+      return *reinterpret_cast<const u32x4*>(kl + off);
+    };
+    u32x4 ring[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) ring[i] = load(L0 + i);
+    if constexpr (kPV) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const u32x4 a = ring[i % kRing];
+        if (i + kRing < L1) ring[i % kRing] = load(i + kRing);
+        const int kb = i >> 3, t2 = (i >> 2) & 1, db = i & 3;
+        const u32x4 pb = {__float_as_uint(sacc[kb][4 * t2]), __float_as_uint(sacc[kb][4 * t2 + 1]),
+                          __float_as_uint(sacc[kb][4 * t2 + 2]), __float_as_uint(sacc[kb][4 * t2 + 3])};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb),
+                                                           oacc[db], 0, 0, 0);
+      }
+    }
+    if constexpr (kQK) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int La = 32 + 2 * j;
+        const u32x4 a0 = ring[La % kRing], a1 = ring[(La + 1) % kRing];
+        if (La + kRing < L1) ring[La % kRing] = load(La + kRing);
+        if (La + 1 + kRing < L1) ring[(La + 1) % kRing] = load(La + 1 + kRing);
+        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        const int s = j >> 2, kb = j & 3;
+        // zero scale operands select the unscaled E4M3 x E4M3 instruction
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[s], s == 0 ? f32x16{} : sacc[kb], 0, 0, 0,
+                                                                   0, 0, 0);
+      }
+    }
+    // Keep the order: the refills for a slot go out right after the MFMA
+    // that consumed it.
+    __builtin_amdgcn_sched_group_barrier(0x100, kPV ? 2 * kRing : kRing, 0);
+    if constexpr (kPV) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kRing < 32)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (i + kRing < L1)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    if constexpr (kQK) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (32 + 2 * j + 1 + kRing < L1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+  };
+
   // ---- softmax phase of tile kt: row maximum, this wave's half of the
   // vote, the vote group's decision (the partner wave runs the same phase in
   // the same slot and publishes through LDS), and for a kept tile the
@@ -369,7 +499,14 @@ void ssa_fwd_kernel(const Params p) {
           mx = __builtin_elementwise_maximum(mx, sacc[kb][r]);
         }
     }
-    const float tmax = scaled_max(halves_max(mx), p.scale);
+    // Factor from accumulator units to scores (one product per row and tile
+    // for FP8 scores, rounded once; the vote uses it exactly as below).
+    float sfac = p.scale, sfac_log2e = p.scale_log2e;
+    if constexpr (kFp8) {
+      sfac = sq_row * kscale_lds[kt];
+      sfac_log2e = sfac * kLog2e;
+    }
+    const float tmax = scaled_max(halves_max(mx), sfac);
     const float dmargin = vote_margin(tmax, m_run);
     bool skip = false;
     if (vote || kDebug) {
@@ -439,8 +576,8 @@ void ssa_fwd_kernel(const Params p) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int r = 8 * t2 + 2 * w;
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], p.scale_log2e, -mb_ref));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], p.scale_log2e, -mb_ref));
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sfac_log2e, -mb_ref));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], sfac_log2e, -mb_ref));
           rs += e0 + e1;
           sacc[kb][4 * t2 + w] = __uint_as_float(pack_bf16(e0, e1));
         }
@@ -457,7 +594,7 @@ void ssa_fwd_kernel(const Params p) {
   // buffers, at the end of its softmax phase in slot 2j, and waits for them
   // at the end of slot 2j + 1.
   if (tid < kWaves) vote_lds[tid] = -2;
-  copy_block(rk, 0, lds_k[0], wave);
+  copy_k(0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   const int nslots = 2 * nkt + 2;
@@ -467,12 +604,22 @@ void ssa_fwd_kernel(const Params p) {
       const int kt = my >> 1;
       if ((my & 1) == 0) {
         if (kt < nkt) {
-          if (p_ready)
-            mfma_phase(std::true_type{}, std::true_type{}, kt);
-          else
-            mfma_phase(std::false_type{}, std::true_type{}, kt);
+          if constexpr (kFp8) {
+            if (p_ready)
+              mfma_phase8(std::true_type{}, std::true_type{}, kt);
+            else
+              mfma_phase8(std::false_type{}, std::true_type{}, kt);
+          } else {
+            if (p_ready)
+              mfma_phase(std::true_type{}, std::true_type{}, kt);
+            else
+              mfma_phase(std::false_type{}, std::true_type{}, kt);
+          }
         } else if (p_ready) {
-          mfma_phase(std::true_type{}, std::false_type{}, kt);
+          if constexpr (kFp8)
+            mfma_phase8(std::true_type{}, std::false_type{}, kt);
+          else
+            mfma_phase(std::true_type{}, std::false_type{}, kt);
         }
         p_ready = false;
       } else if (kt < nkt) {
@@ -481,8 +628,8 @@ void ssa_fwd_kernel(const Params p) {
     }
     if (group_b && (slot & 1) == 0) {
       const int j = slot >> 1;
-      if (j + 1 < nkt) copy_block(rk, j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
-      if (j + 1 < nkt) copy_block(rk, j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
+      if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
+      if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
       if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4));
       if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4) + 1);
     }
@@ -696,6 +843,89 @@ __global__ __launch_bounds__(256) void tile_means_kernel(const uint16_t* __restr
   }
 }
 
+// ---- FP8 (OCP E4M3) quantisation of the score operands -----------------------
+// Each value is divided by its block's scale (IEEE float32 division), clamped
+// to +-448 and rounded to the nearest E4M3 code (ties to even) by
+// v_cvt_pk_fp8_f32.  Scales map the block's largest magnitude to 448:
+// scale = amax / 448 (float32 division), or 1 for an all-zero block.
+constexpr float kE4m3Max = 448.f;
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+}
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -kE4m3Max), kE4m3Max); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Q: one scale per token.  16 lanes per row, 8 channels per lane.
+__global__ __launch_bounds__(256) void quant_q_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ q8,
+                                                        float* __restrict__ qs, long long rows) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int g = threadIdx.x & 15;
+  const bool ok = row < rows;
+  u32x4 x = {0u, 0u, 0u, 0u};
+  if (ok) x = *reinterpret_cast<const u32x4*>(q + row * kD + 8 * g);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bf16_lo(x[e]);
+    f[2 * e + 1] = bf16_hi(x[e]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));   // within the row's 16 lanes
+  const float s = amax > 0.f ? amax / kE4m3Max : 1.f;
+  uint2 w;
+  w.x = e4m3x4(clamp448(f[0] / s), clamp448(f[1] / s), clamp448(f[2] / s), clamp448(f[3] / s));
+  w.y = e4m3x4(clamp448(f[4] / s), clamp448(f[5] / s), clamp448(f[6] / s), clamp448(f[7] / s));
+  if (ok) {
+    *reinterpret_cast<uint2*>(q8 + row * kD + 8 * g) = w;
+    if (g == 0) qs[row] = s;
+  }
+}
+
+// K: one scale per tile of 128 keys.  One workgroup per tile; lane group
+// g = t % 16 holds channels 8 g .. 8 g + 7 of the keys t / 16 + 16 i.
+__global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t* __restrict__ k, uint8_t* __restrict__ k8,
+                                                        float* __restrict__ ks, int H, int S) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nkt = (S + kBK - 1) / kBK;
+  const int g = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const long long row0 = ((long long)b * H + h) * S + (long long)t * kBK;
+  const int n = min(kBK, S - kBK * t);
+  u32x4 x[kBK / 16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kBK / 16; ++i) {
+    const int key = r + 16 * i;
+    x[i] = u32x4{0u, 0u, 0u, 0u};
+    if (key < n) x[i] = *reinterpret_cast<const u32x4*>(k + (row0 + key) * kD + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(x[i][e])), fabsf(bf16_hi(x[i][e]))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.f ? amax / kE4m3Max : 1.f;
+#pragma unroll
+  for (int i = 0; i < kBK / 16; ++i) {
+    const int key = r + 16 * i;
+    uint2 w;
+    w.x = e4m3x4(clamp448(bf16_lo(x[i][0]) / s), clamp448(bf16_hi(x[i][0]) / s), clamp448(bf16_lo(x[i][1]) / s),
+                 clamp448(bf16_hi(x[i][1]) / s));
+    w.y = e4m3x4(clamp448(bf16_lo(x[i][2]) / s), clamp448(bf16_hi(x[i][2]) / s), clamp448(bf16_lo(x[i][3]) / s),
+                 clamp448(bf16_hi(x[i][3]) / s));
+    if (key < n) *reinterpret_cast<uint2*>(k8 + (row0 + key) * kD + 8 * g) = w;
+  }
+  if (threadIdx.x == 0) ks[((long long)b * H + h) * nkt + t] = s;
+}
+
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
@@ -790,9 +1020,9 @@ int resolve(int mode, double p0, double p1, double p2, int seqlen, float* ln_lam
   return SSA_OK;
 }
 
-template <bool kDebug, bool kComp = false>
+template <bool kDebug, bool kComp = false, bool kFp8 = false>
 int launch(const Params& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((ssa_fwd_kernel<kDebug, kComp>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((ssa_fwd_kernel<kDebug, kComp, kFp8>), grid, dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SSA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SSA_OK;
@@ -913,6 +1143,84 @@ int ssa_fwd_virtual(const void* q, const void* k, const void* v, void* o, float*
   if (workspace == nullptr) return fail(SSA_ERR_INVALID_ARG, "workspace must not be NULL");
   return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, nullptr,
                    nullptr, stream, false, workspace, workspace_bytes);
+}
+
+int ssa_quantize_qk_fp8(const void* q, const void* k, uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale,
+                        int B, int H, int S, int D, void* stream) {
+  if (q == nullptr || k == nullptr || q8 == nullptr || k8 == nullptr || q_scale == nullptr || k_scale == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "q, k, q8, k8, q_scale and k_scale must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q8, 8) || !aligned(k8, 8) || !aligned(q_scale, 4) ||
+      !aligned(k_scale, 4))
+    return fail(SSA_ERR_INVALID_ARG, "q, k must be 16-byte, q8, k8 8-byte and the scales 4-byte aligned");
+  if (D != kD) return fail(SSA_ERR_UNSUPPORTED, "head dimension %d is not supported (only 128)", D);
+  if (B < 0 || H < 0 || S < 0) return fail(SSA_ERR_INVALID_ARG, "negative batch, head count or length");
+  if (B > 65535 || H > 65535) return fail(SSA_ERR_UNSUPPORTED, "batch or head count above 65535");
+  if (B == 0 || H == 0 || S == 0) return SSA_OK;
+  const int st = check_device();
+  if (st != SSA_OK) return st;
+  const long long rows = (long long)B * H * S;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(quant_q_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(q), q8, q_scale, rows);
+  hipLaunchKernelGGL(quant_k_kernel, dim3((S + kBK - 1) / kBK, H, B), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(k), k8, k_scale, H, S);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SSA_ERR_LAUNCH, "quantisation launch failed: %s", hipGetErrorString(e));
+  return SSA_OK;
+}
+
+int ssa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const float* q_scale, const float* k_scale, const void* v,
+                void* o, float* lse, int B, int H, int S, int D, float scale, int mode, double p0, double p1,
+                double p2, int seqlen, int32_t* skip_counts, uint8_t* tile_mask, float* tile_margin, void* stream) {
+  if (q8 == nullptr || k8 == nullptr || q_scale == nullptr || k_scale == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "q8, k8, q_scale and k_scale must not be NULL");
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(q_scale, 4) || !aligned(k_scale, 4))
+    return fail(SSA_ERR_INVALID_ARG, "q8, k8 must be 16-byte and the scales 4-byte aligned");
+  int st = check_tensors(v, v, v, o, lse, H, D, scale);
+  if (st != SSA_OK) return st;
+  if (B < 0 || S < 0) return fail(SSA_ERR_INVALID_ARG, "negative batch or sequence length");
+  if (B > 65535) return fail(SSA_ERR_UNSUPPORTED, "batch above 65535");
+  if (((long long)S + kBK) * kRowBytes + kRowBytes >= (1LL << 32))
+    return fail(SSA_ERR_UNSUPPORTED, "sequence length %d too large", S);
+  if ((S + kBK - 1) / kBK > kMaxTilesFp8)
+    return fail(SSA_ERR_UNSUPPORTED, "FP8 scores support at most %d key tiles (S <= %d)", kMaxTilesFp8,
+                kMaxTilesFp8 * kBK);
+  if (skip_counts != nullptr && !aligned(skip_counts, 4)) return fail(SSA_ERR_INVALID_ARG, "skip_counts must be 4-byte aligned");
+  if (tile_margin != nullptr && !aligned(tile_margin, 4)) return fail(SSA_ERR_INVALID_ARG, "tile_margin must be 4-byte aligned");
+  if (tile_margin != nullptr && tile_mask == nullptr) return fail(SSA_ERR_INVALID_ARG, "tile_margin needs tile_mask");
+  Params p{};
+  st = resolve(mode, p0, p1, p2, seqlen, &p.ln_lambda, &p.vote);
+  if (st != SSA_OK) return st;
+  if (B == 0 || H == 0 || S == 0) return SSA_OK;
+  st = check_device();
+  if (st != SSA_OK) return st;
+  p.q = static_cast<const uint16_t*>(v);   // bf16 Q and K are not read on this path
+  p.k = static_cast<const uint16_t*>(v);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.q8 = q8;
+  p.k8 = k8;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.lse = lse;
+  p.counts = skip_counts;
+  p.mask = tile_mask;
+  p.margin = tile_margin;
+  p.nseq = B;
+  p.H = H;
+  p.S = S;
+  p.qgroups = (S + kRowsPerWG - 1) / kRowsPerWG;
+  if ((long long)p.qgroups * H * B >= (1LL << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "more than 2^31 workgroups (B x H x ceil(S / %d))", kRowsPerWG);
+  p.tok_stride = kD;
+  p.head_stride = (long long)S * kD;
+  p.seq_stride = (long long)H * S * kD;
+  p.scale = scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.lambda_per_seq = 0;
+  const dim3 grid(p.qgroups, H, B);
+  return tile_mask != nullptr ? launch<true, false, true>(p, grid, static_cast<hipStream_t>(stream))
+                              : launch<false, false, true>(p, grid, static_cast<hipStream_t>(stream));
 }
 
 int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,

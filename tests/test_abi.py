@@ -142,3 +142,21 @@ def test_virtual_argument_errors(lib):
     assert "smaller" in lib.ssa_last_error().decode()
     assert call(S=2048 * 128 + 1, ws_bytes=1 << 40) == UNSUPPORTED   # more than 2048 key tiles
     assert call(p0=-1.0) == BAD_THRESHOLD
+
+
+def test_fp8_argument_errors(lib):
+    def quant(q=FAKE, q8=FAKE, D=128, S=256):
+        return lib.ssa_quantize_qk_fp8(q, FAKE, q8, FAKE, FAKE, FAKE, 1, 2, S, D, None)
+    assert quant(q=None) == INVALID
+    assert quant(q8=FAKE + 4) == INVALID                    # codes need 8-byte alignment
+    assert quant(D=64) == UNSUPPORTED
+    assert quant(S=0) == OK                                 # empty call
+
+    def fwd(S=256, mask=None, margin=None, p0=1.0, D=128):
+        return lib.ssa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, S, D, 0.088, 0, p0, 0.0, 0.0,
+                               max(S, 1), None, mask, margin, None)
+    assert fwd(D=64) == UNSUPPORTED
+    assert fwd(S=4096 * 128 + 1) == UNSUPPORTED             # more than 4096 key tiles
+    assert fwd(margin=FAKE) == INVALID                      # margin without mask
+    assert fwd(p0=float("nan")) == BAD_THRESHOLD
+    assert fwd(S=0) == OK

@@ -1,0 +1,181 @@
+"""FP8 scores (quantize_qk_fp8 + fwd_fp8) against the CPU oracle.
+
+The quantiser is integer work: codes and scales must equal the oracle's
+(oracle/fp8.py) bit for bit.  The attention is compared with the oracle's
+recurrence run on the dequantised operands.  The E4M3 MFMA does not sum its
+products exactly: on the box it was measured to stay within about 2^-12 of
+the sum of the products' magnitudes (random codes over the full range).  The
+bound used here is EPS = 2^-10 of that sum, per score (oracle.fp8.score_error_bound):
+  * mask: identical to the oracle outside a band of 1e-3 plus twice the largest
+    bound of the block's rows (the margin is a difference of two scores);
+  * O: against the oracle forced to the GPU's mask, the bars of tests/parity.py;
+  * LSE: within 1e-3 plus twice the row's bound.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as ofp8
+from skip_softmax_flashattention_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+EPS = 2.0 ** -10
+
+
+@pytest.fixture(scope="module")
+def ssa():
+    import skip_softmax_flashattention_amd as m
+    m.device_check()
+    return m
+
+
+def _check_quant(ssa, w, heads=None, rows=None, tiles=None):
+    q, k = w.q.cuda(), w.k.cuda()
+    q8, k8, qs, ks = (t.cpu().numpy() for t in ssa.quantize_qk_fp8(q, k))
+    B, H, S, D = w.q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    out = {}
+    for (b, h) in heads:
+        ref = ofp8.quantize_head(oracle.from_bf16(w.q[b, h]), oracle.from_bf16(w.k[b, h]))
+        r = np.arange(S) if rows is None else rows
+        t = np.arange(ks.shape[2]) if tiles is None else tiles
+        assert (q8[b, h][r] == ref.q_codes[r]).all(), f"q codes differ in head {(b, h)}"
+        assert (qs[b, h][r] == ref.q_scale[r]).all(), f"q scales differ in head {(b, h)}"
+        assert (ks[b, h][t] == ref.k_scale[t]).all(), f"k scales differ in head {(b, h)}"
+        for ti in t:
+            sl = slice(128 * ti, min(S, 128 * (ti + 1)))
+            assert (k8[b, h][sl] == ref.k_codes[sl]).all(), f"k codes differ in head {(b, h)} tile {ti}"
+        out[(b, h)] = ref
+    return out
+
+
+def _check_attention(ssa, w, name, qblocks=None, heads=None, **kw):
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    B, H, S, D = q.shape
+    print(f"[case] {name} shape={tuple(q.shape)} {kw}", flush=True)
+    q8, k8, qs, ks = ssa.quantize_qk_fp8(q, k)
+    o, lse, cnt = ssa.fwd_fp8(q8, k8, qs, ks, v, scale=w.scale, **kw)
+    o2, lse2, cnt2, mask, _ = ssa.fwd_fp8(q8, k8, qs, ks, v, scale=w.scale, debug=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(cnt, cnt2), "product and debug entries differ"
+    mask = mask.cpu().numpy().astype(bool)
+    assert (cnt.cpu().numpy() == mask.sum(-1)).all()
+    n = S if kw.get("seqlen") is None else kw["seqlen"]
+    if kw.get("threshold") is not None:
+        lam = oracle.resolve_lambda(threshold=kw["threshold"])
+    else:
+        lam = oracle.resolve_lambda(factor=kw["factor"], seqlen=n)
+    ln = oracle.ln_lambda_f32(lam)
+    o_np, lse_np = o.float().cpu().numpy(), lse.cpu().numpy()
+    nqb = mask.shape[2]
+    qbs = np.arange(nqb) if qblocks is None else np.asarray(qblocks)
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    errs, lerr_over, exempt, worst_bound = [], [], 0, 0.0
+    for (b, h) in heads:
+        ops = ofp8.quantize_head(oracle.from_bf16(w.q[b, h]), oracle.from_bf16(w.k[b, h]))
+        vd = oracle.from_bf16(w.v[b, h])
+        rows = (qbs[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+        valid = rows < S
+        bound_rows = np.zeros(rows.shape)
+        bound_rows[valid] = ofp8.score_error_bound(ops, w.scale, rows[valid], EPS).max(axis=1)
+        worst_bound = max(worst_bound, float(bound_rows.max()))
+        own = oracle.skip_head(ops.q, ops.k, vd, w.scale, ln, qblocks=qbs)
+        gm = mask[b, h][qbs]
+        if ln is not None:
+            band = 1e-3 + 2 * bound_rows.reshape(len(qbs), 64).max(axis=1)[:, None]
+            near = np.abs(own.margin.astype(np.float64) - float(ln)) <= band
+            bad = (gm != own.skipped) & ~near
+            assert not bad.any(), f"{int(bad.sum())} tile decisions differ outside the band"
+            exempt += int((near & (gm != own.skipped)).sum())
+        forced = oracle.skip_head(ops.q, ops.k, vd, w.scale, None, qblocks=qbs, forced_skip=gm)
+        o_ref = forced.o.reshape(-1, D)[valid]
+        lse_ref = forced.lse.reshape(-1)[valid]
+        errs.append(np.abs(o_np[b, h][rows[valid]] - o_ref))
+        lerr_over.append(np.abs(lse_np[b, h][rows[valid]] - lse_ref) - (1e-3 + 2 * bound_rows[valid]))
+    err = np.concatenate(errs)
+    lover = np.concatenate(lerr_over)
+    print(f"[case] {name}: skipped {int(mask.sum())}/{mask.size} exempt {exempt}, max|dO| {err.max():.2e} "
+          f"mean|dO| {err.mean():.2e}, max(|dLSE| - tol) {lover.max():.2e}, largest score bound {worst_bound:.2e}",
+          flush=True)
+    assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
+    assert err.max() <= parity.O_MAX and err.mean() <= parity.O_MEAN
+    assert lover.max() <= 0.0
+    return mask
+
+
+def test_quantize_tiny(ssa):
+    _check_quant(ssa, inputs.tiny())
+
+
+@pytest.mark.parametrize("grid", [(3, 10, 13), (5, 9, 23)])
+def test_quantize_ragged(ssa, grid):
+    w = inputs.grid_small(21, grid, heads=3)
+    _check_quant(ssa, w)
+
+
+def test_quantize_zero_and_extreme_rows(ssa):
+    """An all-zero token (scale 1, codes 0), a token of one huge value and a
+    key tile of tiny values."""
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((1, 1, 300, 128))
+    k = rng.standard_normal((1, 1, 300, 128))
+    q[0, 0, 5] = 0.0
+    q[0, 0, 6] = 1e-3 * rng.standard_normal(128)
+    q[0, 0, 6, 3] = 300.0
+    k[0, 0, 128:256] *= 1e-4
+    t = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    w = inputs.Workload("extreme", t(q), t(k), t(k))
+    _check_quant(ssa, w)
+
+
+@pytest.mark.parametrize("factor", [0.0, 4.0])
+def test_fp8_tiny(ssa, factor):
+    m = _check_attention(ssa, inputs.tiny(), "fp8 tiny", factor=factor)
+    if factor == 0.0:
+        assert not m.any()
+
+
+@pytest.mark.parametrize("grid,factor", [((3, 10, 13), 0.05), ((4, 16, 16), 0.5), ((5, 9, 23), 20.0)])
+def test_fp8_grid(ssa, grid, factor):
+    w = inputs.grid_small(23, grid, heads=2)
+    S = w.q.shape[2]
+    m = _check_attention(ssa, w, f"fp8 grid {grid}", factor=factor * S)
+    assert m.any()
+
+
+def test_fp8_lambda_above_one(ssa):
+    w = inputs.grid_small(24, (4, 12, 20), heads=2)
+    _check_attention(ssa, w, "fp8 lambda > 1", threshold=3.0)
+
+
+def test_fp8_wan_like_sampled(ssa):
+    """The full Wan-like problem: sampled tokens and tiles of the quantiser,
+    sampled query blocks of the attention, and the FP8 output's distance to
+    the bf16 path's (reported)."""
+    w = inputs.wan()
+    S = w.q.shape[2]
+    rng = np.random.default_rng(25)
+    rows = np.sort(rng.choice(S, 2000, replace=False))
+    tiles = np.sort(rng.choice(-(-S // 128), 24, replace=False))
+    tiles[-1] = -(-S // 128) - 1
+    _check_quant(ssa, w, heads=[(0, 0), (0, 21), (0, 39)], rows=rows, tiles=tiles)
+    lam = json.load(open(os.path.join(GOLDEN, "wan_lambdas.json")))["lambda"]["0.75"]
+    qbs = np.sort(rng.choice(-(-S // 64), 5, replace=False))
+    qbs[-1] = -(-S // 64) - 1
+    _check_attention(ssa, w, "fp8 wan-like", qblocks=qbs, heads=[(0, 0), (0, 39)], factor=lam * S)
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    q8, k8, qs, ks = ssa.quantize_qk_fp8(q, k)
+    o8, _, c8 = ssa.fwd_fp8(q8, k8, qs, ks, v, scale=w.scale, factor=lam * S)
+    ob, _, cb = ssa.fwd(q, k, v, scale=w.scale, factor=lam * S)
+    od, _, _ = ssa.fwd(q, k, v, scale=w.scale, factor=0.0)
+    torch.cuda.synchronize()
+    den = od.float().abs().sum()
+    print(f"[case] wan-like: skipped fp8 {int(c8.sum())} bf16 {int(cb.sum())}; rel-L1 to bf16 dense: fp8 "
+          f"{float((o8.float() - od.float()).abs().sum() / den):.4e}, bf16 {float((ob.float() - od.float()).abs().sum() / den):.4e}",
+          flush=True)
