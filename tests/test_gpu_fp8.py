@@ -179,3 +179,18 @@ def test_fp8_wan_like_sampled(ssa):
     print(f"[case] wan-like: skipped fp8 {int(c8.sum())} bf16 {int(cb.sum())}; rel-L1 to bf16 dense: fp8 "
           f"{float((o8.float() - od.float()).abs().sum() / den):.4e}, bf16 {float((ob.float() - od.float()).abs().sum() / den):.4e}",
           flush=True)
+
+
+def test_fp8_long_sampled(ssa):
+    """Long-sequence workload (S = 36864, H = 24, 2% sink keys scaled x4): the
+    quantiser on sampled tokens and tiles, the attention on sampled blocks at
+    threshold 1e-3."""
+    w = inputs.long_seq()
+    S = w.q.shape[2]
+    rng = np.random.default_rng(26)
+    rows = np.sort(rng.choice(S, 2000, replace=False))
+    tiles = np.sort(rng.choice(-(-S // 128), 24, replace=False))
+    _check_quant(ssa, w, heads=[(0, 0), (0, 23)], rows=rows, tiles=tiles)
+    qbs = np.sort(rng.choice(-(-S // 64), 5, replace=False))
+    qbs[-1] = -(-S // 64) - 1
+    _check_attention(ssa, w, "fp8 long", qblocks=qbs, heads=[(0, 0), (0, 23)], threshold=1e-3)

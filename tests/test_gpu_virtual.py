@@ -146,3 +146,14 @@ def test_virtual_wan_like_sampled(ssa):
     rel_skip = float((os_.float() - od.float()).abs().sum() / den)
     rel_virt = float((ov.float() - od.float()).abs().sum() / den)
     print(f"[case] wan-like rel-L1 to dense: skip {rel_skip:.4e}, virtual tiles {rel_virt:.4e}", flush=True)
+
+
+def test_virtual_long_sampled(ssa):
+    """Long-sequence workload (S = 36864, H = 24, 2% sink keys) at threshold
+    1e-3: sampled query blocks of two heads against the oracle."""
+    w = inputs.long_seq()
+    S = w.q.shape[2]
+    rng = np.random.default_rng(16)
+    qbs = np.sort(rng.choice(-(-S // 64), 5, replace=False))
+    qbs[-1] = -(-S // 64) - 1
+    _check(ssa, w, "virtual long", qblocks=qbs, heads=[(0, 0), (0, 23)], threshold=1e-3)
