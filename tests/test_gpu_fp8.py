@@ -69,6 +69,9 @@ def _check_attention(ssa, w, name, qblocks=None, heads=None, **kw):
     n = S if kw.get("seqlen") is None else kw["seqlen"]
     if kw.get("threshold") is not None:
         lam = oracle.resolve_lambda(threshold=kw["threshold"])
+    elif kw.get("calib") is not None:
+        a, bb, ts = kw["calib"]
+        lam = oracle.resolve_lambda(a=a, b=bb, target_sparsity=ts, seqlen=n)
     else:
         lam = oracle.resolve_lambda(factor=kw["factor"], seqlen=n)
     ln = oracle.ln_lambda_f32(lam)
@@ -194,3 +197,19 @@ def test_fp8_long_sampled(ssa):
     qbs = np.sort(rng.choice(-(-S // 64), 5, replace=False))
     qbs[-1] = -(-S // 64) - 1
     _check_attention(ssa, w, "fp8 long", qblocks=qbs, heads=[(0, 0), (0, 23)], threshold=1e-3)
+
+
+def _batched(seed):
+    a, b = inputs.grid_small(seed, (4, 12, 20), heads=2), inputs.grid_small(seed + 1, (4, 12, 20), heads=2)
+    return inputs.Workload("grid batch 2", torch.cat([a.q, b.q]), torch.cat([a.k, b.k]), torch.cat([a.v, b.v]))
+
+
+@pytest.mark.parametrize("control", ["threshold", "calib", "seqlen"])
+def test_fp8_batched_controls(ssa, control):
+    """B = 2 with each threshold control, including a seqlen other than S."""
+    w = _batched(27)
+    S = w.q.shape[2]
+    kw = {"threshold": dict(threshold=0.01), "calib": dict(calib=(2.05276, 13.2810, 0.5)),
+          "seqlen": dict(factor=0.02 * S, seqlen=2 * S)}[control]
+    m = _check_attention(ssa, w, f"fp8 batched {control}", **kw)
+    assert m.any()

@@ -157,3 +157,15 @@ def test_virtual_long_sampled(ssa):
     qbs = np.sort(rng.choice(-(-S // 64), 5, replace=False))
     qbs[-1] = -(-S // 64) - 1
     _check(ssa, w, "virtual long", qblocks=qbs, heads=[(0, 0), (0, 23)], threshold=1e-3)
+
+
+@pytest.mark.parametrize("control", ["threshold", "calib", "seqlen"])
+def test_virtual_batched_controls(ssa, control):
+    """B = 2 with each threshold control, including a seqlen other than S."""
+    a, b = inputs.grid_small(33, (4, 12, 20), heads=2), inputs.grid_small(34, (4, 12, 20), heads=2)
+    w = inputs.Workload("grid batch 2", torch.cat([a.q, b.q]), torch.cat([a.k, b.k]), torch.cat([a.v, b.v]))
+    S = w.q.shape[2]
+    kw = {"threshold": dict(threshold=0.01), "calib": dict(calib=(2.05276, 13.2810, 0.5)),
+          "seqlen": dict(factor=0.02 * S, seqlen=2 * S)}[control]
+    mask, _, _ = _check(ssa, w, f"virtual batched {control}", **kw)
+    assert mask.any()
