@@ -213,3 +213,10 @@ def test_fp8_batched_controls(ssa, control):
           "seqlen": dict(factor=0.02 * S, seqlen=2 * S)}[control]
     m = _check_attention(ssa, w, f"fp8 batched {control}", **kw)
     assert m.any()
+
+
+@pytest.mark.parametrize("S", [1, 63, 129, 300])
+def test_fp8_edge_lengths(ssa, S):
+    """Shorter than a query block, one key past a tile, ragged in both."""
+    w = inputs.random_qkv(200 + S, 2, 3, S, qk_gain=2.0)
+    _check_attention(ssa, w, f"fp8 edge S={S}", factor=0.3 * S)

@@ -169,3 +169,10 @@ def test_virtual_batched_controls(ssa, control):
           "seqlen": dict(factor=0.02 * S, seqlen=2 * S)}[control]
     mask, _, _ = _check(ssa, w, f"virtual batched {control}", **kw)
     assert mask.any()
+
+
+@pytest.mark.parametrize("S", [1, 63, 129, 300])
+def test_virtual_edge_lengths(ssa, S):
+    """Shorter than a query block, one key past a tile, ragged in both."""
+    w = inputs.random_qkv(200 + S, 2, 3, S, qk_gain=2.0)
+    _check(ssa, w, f"virtual edge S={S}", factor=0.3 * S)
