@@ -524,12 +524,12 @@ void ssa_fwd_kernel(const Params p) {
       if (lane == 0)
         __hip_atomic_store(&vote_lds[wave], (kt << 1) | (own_pass ? 1 : 0), kPub, __HIP_MEMORY_SCOPE_WORKGROUP);
       // The partner publishes in this same slot; the bound only guards
-      // against a wave that never arrives.
+      // against a wave that never arrives.  Each poll is one LDS round trip;
+      // sleeping between polls measured slightly slower.
       int pv = 0;
       for (int spin = 0; spin < kSpinLimit; ++spin) {
         pv = __hip_atomic_load(&vote_lds[wave ^ 1], kSub, __HIP_MEMORY_SCOPE_WORKGROUP);
         if ((pv >> 1) == kt) break;
-        __builtin_amdgcn_s_sleep(1);
       }
       skip = vote && own_pass && (pv & 1) != 0;
       if constexpr (kDebug) {
