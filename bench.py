@@ -63,15 +63,14 @@ def issued_mfma_flops(mask, D=128, bq=64, bk=128):
 
 
 def cpu_baseline(w, ln_lambda, seconds):
-    """The oracle's recurrence on seeded query blocks of the workload's heads
-    (whole heads in order, then part of the next), sized to about ``seconds``."""
+    """The oracle's recurrence (the plain-C oracle: single precision, OpenMP
+    over query blocks on every host core it is given) on seeded query blocks
+    of the workload's heads, whole heads in order, sized to about ``seconds``."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
-    except Exception:
-        cores = os.cpu_count() or 1
+    from oracle import c_oracle
+    orc = c_oracle.oracle()
+    cores = orc.threads()
     S = w.q.shape[2]
     nqb = -(-S // 64)
     c = np.minimum(128, S - 128 * np.arange(-(-S // 128))).astype(np.float64)
@@ -80,28 +79,29 @@ def cpu_baseline(w, ln_lambda, seconds):
         qd, kd, vd = (oracle.from_bf16(t[0, h]) for t in (w.q, w.k, w.v))
         qbs = np.sort(rng.choice(nqb, n, replace=False))
         t0 = time.perf_counter()
-        r = oracle.skip_head(qd, kd, vd, w.scale, ln_lambda, qblocks=qbs)
+        r = orc.skip_head(qd, kd, vd, w.scale, ln_lambda, qblocks=qbs)
         dt = time.perf_counter() - t0
         rows = np.minimum(64, S - 64 * qbs).astype(np.float64)
         return dt, 2.0 * 128 * (rows[:, None] * c[None, :] * (1 + (~r.skipped))).sum()
 
     rng = np.random.default_rng(7)
-    dt0, _ = run_head(0, 2, rng)
-    per_block = dt0 / 2
+    n0 = max(2, cores)
+    dt0, _ = run_head(0, min(n0, nqb), rng)
+    per_block = dt0 / min(n0, nqb)
     budget = int(max(2, round(seconds / max(per_block, 1e-4))))
     tot_dt = tot_fl = 0.0
-    heads = 0
+    heads = blocks = 0
     while budget > 0 and heads < w.q.shape[1]:
         n = min(nqb, budget)
         dt, fl = run_head(heads, n, rng)
         tot_dt += dt
         tot_fl += fl
         budget -= n
+        blocks += n
         heads += 1
-    blocks = int(round(seconds / max(per_block, 1e-4)))
     return {"value": round(tot_fl / tot_dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{min(blocks, nqb * heads)} query blocks (64 rows x all 256 key tiles) over the first {heads} "
-                      f"head(s), seeded, at the same lambda; float64 numpy recurrence, {tot_dt:.1f} s"}
+            "sample": f"{blocks} query blocks (64 rows x all 256 key tiles) over the first {heads} head(s), seeded, "
+                      f"at the same lambda; plain-C float32 recurrence (gcc -O2, OpenMP), {tot_dt:.1f} s"}
 
 
 def copy_reference(launches):

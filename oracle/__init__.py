@@ -3,8 +3,11 @@
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline may use this package; the library and its Python binding never do.
 It is plain numpy in float64 (the skip vote in float32, the kernel's
-precision) and shares no code with the HIP path.
+precision), plus the same method in plain C (c_oracle: softmax attention in
+double precision and the tiled recurrence in single precision, built with
+gcc on first use).  Neither shares code with the HIP path.
 """
+from . import c_oracle  # noqa: F401
 from . import fp8  # noqa: F401
 from .skip_attention import (  # noqa: F401
     BLOCK_K,

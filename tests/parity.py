@@ -39,24 +39,28 @@ class Report:
                 f"max|dLSE| {self.lse_max:.2e}")
 
 
-def compare_head_blocks(qd, kd, vd, scale, ln_lambda, qblocks, gpu_mask, gpu_o, gpu_lse, gpu_counts) -> Report:
+def compare_head_blocks(qd, kd, vd, scale, ln_lambda, qblocks, gpu_mask, gpu_o, gpu_lse, gpu_counts,
+                        ref=None) -> Report:
     """Compare one head's selected q-blocks.  qd/kd/vd: float64 [S, D];
     gpu_mask [nb, nKT] bool; gpu_o [nb*64 rows clipped to S, D]; gpu_lse
-    likewise; gpu_counts [nb]."""
+    likewise; gpu_counts [nb].  ``ref`` is the oracle's skip_head (the
+    float64 Python oracle by default; the single-precision C oracle's
+    skip_head takes the same arguments)."""
     S = qd.shape[0]
-    own = oracle.skip_head(qd, kd, vd, scale, ln_lambda, qblocks=qblocks)
+    ref = oracle.skip_head if ref is None else ref
+    own = ref(qd, kd, vd, scale, ln_lambda, qblocks=qblocks)
     if ln_lambda is None:
         band = np.zeros_like(own.skipped)
     else:
         band = np.abs(own.margin.astype(np.float64) - float(ln_lambda)) <= MASK_BAND
     bad = (gpu_mask != own.skipped) & ~band
     assert not bad.any(), f"{int(bad.sum())} tile decisions differ outside the band (first at {np.argwhere(bad)[:3].tolist()})"
-    forced = own if np.array_equal(gpu_mask, own.skipped) else oracle.skip_head(
+    forced = own if np.array_equal(gpu_mask, own.skipped) else ref(
         qd, kd, vd, scale, None, qblocks=qblocks, forced_skip=gpu_mask)
     rows = (np.asarray(qblocks)[:, None] * oracle.BLOCK_Q + np.arange(oracle.BLOCK_Q)[None, :]).reshape(-1)
     valid = rows < S
-    o_ref = forced.o.reshape(-1, qd.shape[1])[valid]
-    lse_ref = forced.lse.reshape(-1)[valid]
+    o_ref = forced.o.reshape(-1, qd.shape[1])[valid].astype(np.float64)
+    lse_ref = forced.lse.reshape(-1)[valid].astype(np.float64)
     err = np.abs(gpu_o - o_ref)
     lerr = np.abs(gpu_lse - lse_ref)
     assert np.isfinite(gpu_o).all() and np.isfinite(gpu_lse).all()
@@ -81,7 +85,7 @@ def assert_bar(rep: Report):
 
 def check_fixed(ssa, w, *, factor: Optional[float] = None, threshold: Optional[float] = None,
                 calib=None, seqlen: Optional[int] = None, heads: Optional[Sequence] = None,
-                qblocks: Optional[Sequence[int]] = None, device="cuda") -> Report:
+                qblocks: Optional[Sequence[int]] = None, device="cuda", ref=None) -> Report:
     """Run the product entry point and the debug entry point on one fixed-length
     workload and compare with the oracle on the selected (b, h) heads and
     q-blocks (all by default)."""
@@ -116,5 +120,5 @@ def check_fixed(ssa, w, *, factor: Optional[float] = None, threshold: Optional[f
         rows = (qbs[:, None] * oracle.BLOCK_Q + np.arange(oracle.BLOCK_Q)[None, :]).reshape(-1)
         rows = rows[rows < S]
         reports.append(compare_head_blocks(qd, kd, vd, w.scale, ln, qbs, mask[b, h][qbs], o_np[b, h][rows],
-                                           lse_np[b, h][rows], cnt_np[b, h][qbs]))
+                                           lse_np[b, h][rows], cnt_np[b, h][qbs], ref=ref))
     return merge(reports)

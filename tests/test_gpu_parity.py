@@ -34,6 +34,38 @@ def _run(ssa, w, name, **kw):
     return rep
 
 
+# ---- Against the single-precision C oracle ---------------------------------
+# The same bar, with the reference recurrence run in float32 by the plain-C
+# oracle (oracle/skip_attention_c.c) instead of the float64 Python one.
+@pytest.mark.parametrize("factor", [0.0, 0.5, 4.0])
+def test_tiny_vs_fp32_oracle(ssa, factor):
+    from oracle import c_oracle
+    _run(ssa, inputs.tiny(), f"tiny fp32-oracle factor={factor}", factor=factor, ref=c_oracle.oracle().skip_head)
+
+
+@pytest.mark.parametrize("lam", [1e-4, 1e-2])
+def test_mid_vs_fp32_oracle(ssa, lam):
+    from oracle import c_oracle
+    _run(ssa, inputs.mid(), f"mid fp32-oracle lambda={lam}", threshold=lam, heads=[(0, 0), (1, 7)],
+         ref=c_oracle.oracle().skip_head)
+
+
+def test_wan_like_sampled_vs_fp32_oracle(ssa):
+    """Full-size Wan-like problem at the 75%-skip lambda: 16 sampled query
+    blocks (first, last and ragged included) of two heads."""
+    import json
+    import os
+    from oracle import c_oracle
+    w = inputs.wan()
+    S = w.q.shape[2]
+    with open(os.path.join(os.path.dirname(__file__), "golden", "wan_lambdas.json")) as f:
+        lam = json.load(f)["lambda"]["0.75"]
+    nqb = -(-S // 64)
+    qbs = np.unique(np.concatenate([[0, 1, nqb - 1], np.random.default_rng(5).choice(nqb, 13, replace=False)]))
+    _run(ssa, w, "wan-like fp32-oracle sampled", factor=lam * S, heads=[(0, 0), (0, 39)], qblocks=qbs,
+         ref=c_oracle.oracle().skip_head)
+
+
 # ---- Tiny workload: B=1, H=2, S=1024; factor in {0, 0.5, 4.0} ----------------
 @pytest.mark.parametrize("factor", [0.0, 0.5, 4.0])
 def test_tiny(ssa, factor):
