@@ -31,8 +31,9 @@
  * a last key tile shorter than 128 keys is padded with keys of score -inf.
  *
  * Layouts and ownership (all buffers are device memory owned by the caller;
- * the library allocates nothing, never synchronises, and enqueues one kernel
- * on `stream`, a hipStream_t or NULL for the default stream):
+ * the library allocates nothing, never synchronises, and enqueues its work on
+ * `stream`, a hipStream_t or NULL for the default stream: one kernel per
+ * call, two for ssa_fwd_virtual and ssa_quantize_qk_fp8):
  *   q, k, v, o    bf16, [B, H, S, D] contiguous, 16-byte aligned, D = 128.
  *   lse           float [B, H, S]: LSE_i = m_i + ln(l_i), natural log of the
  *                 row's softmax denominator over the kept tiles. May be NULL.
