@@ -1,0 +1,61 @@
+"""The benchmark's contract: the one-JSON-line output, the one-GPU refusal,
+and the FLOP accounting its throughput figures rest on."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_executed_flops_counts_valid_rows_and_keys():
+    """S = 100: q-blocks of 64 and 36 rows, key tiles of 100 keys (one tile).
+    QK^T of both blocks always; P.V only of the kept block."""
+    mask = np.array([[[[True], [False]]]])   # block 0 skips tile 0, block 1 keeps it
+    D = 128
+    want = 2 * D * (64 * 100 + 36 * 100) + 2 * D * (36 * 100)
+    assert bench.executed_flops(mask, 100, D=D) == want
+
+
+def test_executed_flops_dense_equals_the_definition():
+    """No skipped tile: executed work is 4 B H S^2 D, the dense count."""
+    B, H, S, D = 2, 3, 300, 128
+    mask = np.zeros((B, H, -(-S // 64), -(-S // 128)), bool)
+    assert bench.executed_flops(mask, S, D=D) == 4 * B * H * S * S * D
+
+
+def test_issued_mfma_flops_pads_tiles():
+    mask = np.array([[[[True, False], [False, False]]]])
+    assert bench.issued_mfma_flops(mask) == 2 * 128 * 64 * 128 * (4 + 3)
+
+
+@pytest.mark.gpu
+def test_bench_json_line():
+    """A short run prints one JSON line with every field the driver reads."""
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
+                        "--cpu-seconds", "1"], capture_output=True, text=True, timeout=280, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert "workload" in d["config"]
+    roof = d["roofline"]
+    assert roof["bound"] in ("hbm", "mfma", "alu") and roof["unit"] in ("GB/s", "TFLOP/s")
+    assert roof["peak"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    cpu = d["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
