@@ -3,9 +3,9 @@
 Thin ctypes binding of the C ABI in include/ssa.h (libssa.so, built for
 gfx950).  This module only marshals arguments: it checks tensor dtypes,
 shapes and devices, allocates the outputs with torch, and passes raw device
-pointers and the current HIP stream to the library, which enqueues one
-kernel.  Every step of the attention runs in the HIP kernel; there is no
-fallback.  If libssa.so is missing or the device is not gfx950 the calls
+pointers and the current HIP stream to the library, which enqueues its
+kernels (one per call; two for fwd_virtual and quantize_qk_fp8).  Every step
+of the attention runs in the HIP kernels; there is no fallback.  If libssa.so is missing or the device is not gfx950 the calls
 raise.
 
 Controls ("Skip-Softmax" design document of vLLM-Omni, section "From
