@@ -22,7 +22,9 @@
 //   softmax phase  row maximum, the vote group's skip decision, and for a
 //                  kept tile the online-softmax update with P in bf16
 // Group B runs one slot behind group A, so in every slot one wave of each
-// SIMD feeds the matrix cores while the other runs the softmax.
+// SIMD feeds the matrix cores while the other runs the softmax.  A call
+// without the skip test (lambda = 0) runs a separate instance of the kernel
+// whose only difference is which wave issues the V copies, and when.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  S^T is
 // 4 key blocks of 32 x 32: a lane holds one query row and 16 keys per block,
@@ -176,7 +178,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
 
-template <bool kDebug, bool kComp, bool kFp8>
+// kDense: the lambda = 0 instance (no vote); it differs from the general one
+// only in when and by which wave the K/V copies are issued.
+template <bool kDebug, bool kComp, bool kFp8, bool kDense>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssa_fwd_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kFp8 ? kTile8Bytes : kTileBytes];
@@ -225,7 +229,7 @@ void ssa_fwd_kernel(const Params p) {
 
   float ln_lambda = p.ln_lambda;
   if (p.lambda_per_seq) ln_lambda = (float)log(p.factor / (double)S_b);
-  const bool vote = p.vote != 0;
+  const bool vote = !kDense && p.vote != 0;
 
   const int nkt = (S_b + kBK - 1) / kBK;
   const int wrow0 = qg * kRowsPerWG + wave * kRowsPerWave;   // this wave's first row
@@ -307,6 +311,21 @@ void ssa_fwd_kernel(const Params p) {
     if constexpr (kFp8) copy_block8(kt, dst, blk);
     else copy_block(rk, kt, dst, blk);
   };
+  // The dense instance's copies: instruction j of block blk of tile kt (of V
+  // when is_v, else of K) into the LDS tile at byte offset lds_tile, as in
+  // copy_block but through inline assembly.  The compiler does not see these
+  // loads, so it never makes an LDS read of the other buffer wait for them;
+  // the vmcnt(0) at the end of every odd slot is their only wait.
+  const uint32_t lds_k_off = (uint32_t)(uintptr_t)LDS_PTR(unsigned char, &lds_k[0][0]);
+  const uint32_t lds_v_off = (uint32_t)(uintptr_t)LDS_PTR(unsigned char, &lds_v[0][0]);
+  auto copy_one_untracked = [&](bool is_v, int kt, uint32_t lds_tile, int blk, int j) __attribute__((always_inline)) {
+    const uint32_t goff = (uint32_t)(kt * kBK + 16 * blk) * ts_bytes;
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (uint32_t)((16 * blk + 4 * j) * kRowBytes));
+    if (is_v)
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(copy_off[j] + goff), "s"(rv), "{m0}"(m0));
+    else
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(copy_off[j] + goff), "s"(rk), "{m0}"(m0));
+  };
 
   // Per-lane LDS byte offsets of the operand reads.
   // K operand (A of S^T): row 32 kb + key_perm(c), logical chunk 2 s + hf.
@@ -350,10 +369,12 @@ void ssa_fwd_kernel(const Params p) {
   // S^T = K Q^T for tile kt.  One stream of up to 64 MFMAs whose A operands
   // (V^T by transpose reads, then K) come from LDS through one ring of
   // fragments read kRing steps ahead; four independent accumulators in each
-  // half hide the MFMA latency.
+  // half hide the MFMA latency.  With cp_c set (the dense instance, group A)
+  // the QK^T steps also issue the copy of V(kt), one instruction every fourth
+  // MFMA, into the V buffer this phase does not read.
   constexpr int kRing = 8;
-  auto mfma_phase = [&](auto pv_c, auto qk_c, int kt) __attribute__((always_inline)) {
-    constexpr bool kPV = decltype(pv_c)::value, kQK = decltype(qk_c)::value;
+  auto mfma_phase = [&](auto pv_c, auto qk_c, auto cp_c, int kt) __attribute__((always_inline)) {
+    constexpr bool kPV = decltype(pv_c)::value, kQK = decltype(qk_c)::value, kCopy = decltype(cp_c)::value;
     constexpr int n0 = kPV ? 0 : 32, n1 = kQK ? 64 : 32;   // steps [n0, n1): < 32 P.V, >= 32 QK^T
     const unsigned char* vl = lds_v[(kt - 1) & 1];
     const unsigned char* kl = lds_k[kt & 1];
@@ -386,6 +407,14 @@ void ssa_fwd_kernel(const Params p) {
       } else {
         const int s = (i - 32) >> 2, kb = i & 3;
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
+      }
+      if constexpr (kCopy) {
+        // the wave's blocks 2 wave and 2 wave + 1 of V(kt)
+        if (i >= 32 && (i - 32) % 4 == 0) {
+          const int cj = (i - 32) / 4;
+          copy_one_untracked(true, kt, lds_v_off + (uint32_t)((kt & 1) * kTileBytes), 2 * wave + cj / kCopyPerWave,
+                             cj % kCopyPerWave);
+        }
       }
     }
     // Keep the order: reads for step i + kRing go out right after MFMA i.
@@ -591,8 +620,10 @@ void ssa_fwd_kernel(const Params p) {
   // So on every SIMD one wave feeds the matrix cores while the other runs
   // the softmax.  The MFMA phase of tile j reads K(j) and V(j - 1) in slots
   // 2j (A) and 2j + 1 (B); group B copies K(j + 1) and V(j), into the other
-  // buffers, at the end of its softmax phase in slot 2j, and waits for them
-  // at the end of slot 2j + 1.
+  // buffers, at the end of its softmax phase in slot 2j, and every wave waits
+  // for them at the end of slot 2j + 1.  The dense instance moves the V(j)
+  // copy into group A's QK^T steps of slot 2j, so it overlaps MFMA work
+  // instead of stretching group B's softmax phase.
   if (tid < kWaves) vote_lds[tid] = -2;
   copy_k(0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -609,17 +640,25 @@ void ssa_fwd_kernel(const Params p) {
               mfma_phase8(std::true_type{}, std::true_type{}, kt);
             else
               mfma_phase8(std::false_type{}, std::true_type{}, kt);
+          } else if constexpr (kDense) {
+            if (p_ready) {
+              if (group_b) mfma_phase(std::true_type{}, std::true_type{}, std::false_type{}, kt);
+              else mfma_phase(std::true_type{}, std::true_type{}, std::true_type{}, kt);
+            } else {
+              if (group_b) mfma_phase(std::false_type{}, std::true_type{}, std::false_type{}, kt);
+              else mfma_phase(std::false_type{}, std::true_type{}, std::true_type{}, kt);
+            }
           } else {
             if (p_ready)
-              mfma_phase(std::true_type{}, std::true_type{}, kt);
+              mfma_phase(std::true_type{}, std::true_type{}, std::false_type{}, kt);
             else
-              mfma_phase(std::false_type{}, std::true_type{}, kt);
+              mfma_phase(std::false_type{}, std::true_type{}, std::false_type{}, kt);
           }
         } else if (p_ready) {
           if constexpr (kFp8)
             mfma_phase8(std::true_type{}, std::false_type{}, kt);
           else
-            mfma_phase(std::true_type{}, std::false_type{}, kt);
+            mfma_phase(std::true_type{}, std::false_type{}, std::false_type{}, kt);
         }
         p_ready = false;
       } else if (kt < nkt) {
@@ -628,10 +667,20 @@ void ssa_fwd_kernel(const Params p) {
     }
     if (group_b && (slot & 1) == 0) {
       const int j = slot >> 1;
-      if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
-      if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
-      if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4));
-      if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4) + 1);
+      if constexpr (kDense) {
+        // V(j) was issued by group A during its QK^T steps of slot 2j
+        if (j + 1 < nkt) {
+#pragma unroll
+          for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
+            copy_one_untracked(false, j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTileBytes),
+                               2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
+        }
+      } else {
+        if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
+        if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
+        if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4));
+        if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4) + 1);
+      }
     }
     // LDS operations (votes, operand reads) complete before the barrier, so
     // the barrier orders them; a memory fence is not used because it would
@@ -1022,7 +1071,10 @@ int resolve(int mode, double p0, double p1, double p2, int seqlen, float* ln_lam
 
 template <bool kDebug, bool kComp = false, bool kFp8 = false>
 int launch(const Params& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((ssa_fwd_kernel<kDebug, kComp, kFp8>), grid, dim3(kThreads), 0, stream, p);
+  if (!kDebug && !kComp && !kFp8 && p.vote == 0)
+    hipLaunchKernelGGL((ssa_fwd_kernel<false, false, false, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((ssa_fwd_kernel<kDebug, kComp, kFp8, false>), grid, dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SSA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SSA_OK;
