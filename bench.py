@@ -13,8 +13,11 @@ MFMA utilisation against the bf16 dense peak; the dense call's numbers; the
 speedup; a roofline entry for the kernel; the virtual-tile variant
 (fwd_virtual) timed beside the plain skip call with both outputs' relative L1
 distance to dense attention; the FP8-score variant (quantize_qk_fp8 +
-fwd_fp8) at lambda = 0 and at the timed lambda; and the CPU oracle timed on a
-bounded sample as a baseline only.
+fwd_fp8) at lambda = 0 and at the timed lambda; the other configurations
+(``other_configs``: the Wan-like problem at the sweep's other skip fractions,
+the long sequence with sink keys at lambda = 1e-3, the calibrated varlen batch
+at target sparsity 0.5, 0.7 and 0.9), each paired with its own lambda = 0
+call; and the CPU oracle timed on a bounded sample as a baseline only.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15]
 """
@@ -147,7 +150,8 @@ def main():
     ssa.device_check()
     dev = torch.device("cuda:0")
     with open(os.path.join(ROOT, "tests", "golden", "wan_lambdas.json")) as f:
-        lam = json.load(f)["lambda"][str(args.target)]
+        lams = json.load(f)["lambda"]
+    lam = lams[str(args.target)]
     w = inputs.wan()
     q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
     B, H, S, D = q.shape
@@ -275,6 +279,72 @@ def main():
     fp8_skip_frac = float(c8.sum()) / float(mask_np.size)
     del q8, k8, qs8, ks8, c8
 
+    # The other configurations, each timed against its own lambda = 0 call:
+    # the Wan-like problem at the other skip fractions of the sweep, the long
+    # sequence with sink keys at lambda = 1e-3, and the calibrated varlen
+    # batch at each target sparsity.
+    n_side = max(5, args.steps // 4)
+
+    def paired(fd, fs):
+        fd()
+        fs()
+        torch.cuda.synchronize()
+        e = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_side)]
+        for a in e:
+            a[0].record(stream)
+            fd()
+            a[1].record(stream)
+            a[2].record(stream)
+            r = fs()
+            a[3].record(stream)
+        torch.cuda.synchronize()
+        return (float(np.mean([a[0].elapsed_time(a[1]) for a in e])),
+                float(np.mean([a[2].elapsed_time(a[3]) for a in e])), r)
+
+    def leg(td, ts, flops, skipped, tiles):
+        return {"dense_ms": round(td, 4), "skip_ms": round(ts, 4), "skip_fraction": round(skipped / tiles, 4),
+                "dense_mfma_util": round(flops / (td * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "effective_tflops": round(flops / (ts * 1e-3) / 1e12, 2), "speedup_vs_dense": round(td / ts, 4)}
+
+    others = {}
+    for tgt, lam_t in sorted(lams.items()):
+        if abs(float(tgt) - args.target) < 1e-9:
+            continue
+        td, ts, r = paired(dense, lambda: ssa.fwd(q, k, v, factor=lam_t * S, scale=w.scale))
+        others[f"wan_like_skip_{tgt}"] = {"lambda": lam_t, **leg(td, ts, dense_flops, int(r[2].sum()), mask_np.size)}
+
+    wl = inputs.long_seq()
+    ql, kl, vl = (t.to(dev) for t in (wl.q, wl.k, wl.v))
+    Bl, Hl, Sl, _ = ql.shape
+    td, ts, r = paired(lambda: ssa.fwd(ql, kl, vl, factor=0.0, scale=wl.scale),
+                       lambda: ssa.fwd(ql, kl, vl, threshold=1e-3, scale=wl.scale))
+    others["long_seq_threshold_1e-3"] = dict(
+        workload=f"B={Bl} H={Hl} S={Sl} grid 24x32x48, 2% sink keys, seed 3",
+        **leg(td, ts, 4.0 * Bl * Hl * Sl * Sl * D, int(r[2].sum()), Bl * Hl * -(-Sl // 64) * -(-Sl // 128)))
+    del ql, kl, vl, wl
+
+    wv = inputs.varlen()
+    qv, kv, vv = (t.to(dev) for t in (wv.q, wv.k, wv.v))
+    cu, smax, lens = wv.cu_seqlens.to(dev), max(wv.seqlens), wv.seqlens
+    with open(os.path.join(ROOT, "tests", "golden", "varlen_calibration.json")) as f:
+        cal = json.load(f)
+    fl_v = sum(4.0 * qv.shape[1] * n * n * D for n in lens)
+    for tgt in (0.5, 0.7, 0.9):
+        td, ts, r = paired(lambda: ssa.fwd_varlen(qv, kv, vv, cu, smax, factor=0.0, scale=wv.scale),
+                           lambda: ssa.fwd_varlen(qv, kv, vv, cu, smax, calib=(cal["a"], cal["b"], tgt),
+                                                  scale=wv.scale))
+        cnt_v = r[2].cpu().numpy()
+        per_seq, off = [], 0
+        for n in lens:
+            nqb = -(-n // 64)
+            per_seq.append(round(float(cnt_v[:, off:off + nqb].sum()) / (cnt_v.shape[0] * nqb * -(-n // 128)), 4))
+            off += nqb
+        tiles = sum(cnt_v.shape[0] * -(-n // 64) * -(-n // 128) for n in lens)
+        others[f"varlen_calibrated_{tgt}"] = dict(skip_fraction_per_sequence=per_seq,
+                                                  **leg(td, ts, fl_v, int(cnt_v.sum()), tiles))
+    others["varlen_workload"] = f"H={qv.shape[1]} S_b={lens}, calibrated a={cal['a']:.5f} b={cal['b']:.4f}, seed 4"
+    del qv, kv, vv, wv
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -333,6 +403,7 @@ def main():
         "ulysses8_share": {"heads": 5, "dense_ms": round(d5, 4), "skip_ms": round(s5, 4),
                            "dense_mfma_util": round(dense_flops / 8 / (d5 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "speedup_vs_dense": round(d5 / s5, 4)},
+        "other_configs": others,
         "timed_wall_s": round(t_wall, 3),
         "kernel_sha256_16": kernel_hash(),
     }

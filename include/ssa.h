@@ -100,11 +100,14 @@ int ssa_fwd_calibrated(const void* q, const void* k, const void* v, void* o, flo
 /* Packed variable-length batch ("cu_seqlens" layout): sequence b holds the
  * tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, k, v, o, which are bf16
  * [T, H, D] with T = cu_seqlens[nseq].  cu_seqlens: device int32 [nseq + 1],
- * non-decreasing from 0; every length must be <= max_seqlen.  Attention never
+ * non-decreasing from 0; every length must be <= max_seqlen (the kernel
+ * leaves the rows of a sequence whose length is negative or above
+ * max_seqlen unwritten and counts no query block for it).  Attention never
  * crosses sequences and each sequence normalises lambda by its own length
  * S_b (see ssa_mode).  lse: float [H, T] (nullable).  skip_counts: int32
  * [H, sum_b ceil(S_b / 64)], query blocks of sequence b after those of
- * sequences 0..b-1 (nullable). */
+ * sequences 0..b-1 (nullable).  The work is spread so that each of the
+ * eight XCDs gets an eighth of every sequence, whatever the mix of lengths. */
 int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                    const int32_t* cu_seqlens, int nseq, int max_seqlen, int H, int D,
                    float scale, int mode, double p0, double p1, double p2,

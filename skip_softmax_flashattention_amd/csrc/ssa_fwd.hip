@@ -178,6 +178,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
 
+// Packed batches: the number of items sequence sb contributes (0 for a
+// length that is negative or above max_seqlen, or past the last sequence).
+__device__ __forceinline__ int varlen_len(const Params& p, int sb) {
+  int len = sb < p.nseq ? p.cu_seqlens[sb + 1] - p.cu_seqlens[sb] : 0;
+  return (len < 0 || len > p.S) ? 0 : len;
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_incl_sum(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Query blocks (of 64 rows) of the sequences before sequence b, and of all
+// sequences: the offset and row length of the skip-count layout
+// [H, sum_b ceil(S_b / 64)].
+__device__ __forceinline__ void varlen_qblocks(const Params& p, int b, int lane, long long& off, long long& total) {
+  off = 0;
+  total = 0;
+  for (int base0 = 0; base0 < p.nseq; base0 += 64) {
+    const int nqb = (varlen_len(p, base0 + lane) + kBQ - 1) / kBQ;
+    const int incl = wave_incl_sum(nqb, lane);
+    if (b >= base0 && b < base0 + 64)
+      off = total + __builtin_amdgcn_readlane(incl, b - base0) - __builtin_amdgcn_readlane(nqb, b - base0);
+    total += __builtin_amdgcn_readlane(incl, 63);
+  }
+}
+
 // kDense: the lambda = 0 instance (no vote); it differs from the general one
 // only in when and by which wave the K/V copies are issued.
 template <bool kDebug, bool kComp, bool kFp8, bool kDense>
@@ -195,8 +227,13 @@ void ssa_fwd_kernel(const Params p) {
   // contiguous range of the (query group, head, sequence) list: the 32 CUs
   // of an XCD then stream the same head's K/V tiles at the same time and
   // share them in their L2, instead of two heads per XCD at half the reuse.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, hf = lane >> 5;
+  const bool group_b = wave >= 4;
   int qg, h, b;
-  {
+  long long tok0 = 0;
+  int S_b = p.S;
+  if (p.cu_seqlens == nullptr) {
     const int gx = gridDim.x, gy = gridDim.y;
     const int n = gx * gy * (int)gridDim.z;
     const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
@@ -205,16 +242,43 @@ void ssa_fwd_kernel(const Params p) {
     qg = W % gx;
     h = (W / gx) % gy;
     b = W / (gx * gy);
-  }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 31, hf = lane >> 5;
-  const bool group_b = wave >= 4;
-
-  long long tok0 = 0;
-  int S_b = p.S;
-  if (p.cu_seqlens != nullptr) {
+  } else {
+    // Packed batch: sequences differ in length, so equal ranges of a grid
+    // padded to max_seqlen would hand some XCDs all the long sequences.
+    // Sequence b has I_b = H * ceil(S_b / 256) work items in (head, query
+    // group) order; XCD x takes the x-th of eight near-equal contiguous
+    // chunks of every sequence's items, sequences in order, so each XCD gets
+    // an eighth of every sequence (and still whole runs of one head).  The
+    // 1-D grid holds 8 * nseq * ceil(H * ceil(max_seqlen / 256) / 8)
+    // workgroups; those past the end of their XCD's list return at once.
+    // One wave-wide prefix scan per 64 sequences finds this workgroup's
+    // sequence.  Sequences whose length is negative or above max_seqlen get
+    // no items.
+    const int L = blockIdx.x;
+    const int xcd = L % kXcds;
+    int r = L / kXcds;
+    b = -1;
+    int local = 0;
+    for (int base0 = 0; base0 < p.nseq && b < 0; base0 += 64) {
+      const long long items = (long long)p.H * ((varlen_len(p, base0 + lane) + kRowsPerWG - 1) / kRowsPerWG);
+      const int cnt = (int)(items * (xcd + 1) / kXcds - items * xcd / kXcds);
+      const int incl = wave_incl_sum(cnt, lane);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (r < total) {
+        const int ln = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > r));   // first lane past r
+        b = base0 + ln;
+        local = r - (__builtin_amdgcn_readlane(incl, ln) - __builtin_amdgcn_readlane(cnt, ln));
+      } else {
+        r -= total;
+      }
+    }
+    if (b < 0) return;   // nothing left in this XCD's list
     tok0 = p.cu_seqlens[b];
     S_b = p.cu_seqlens[b + 1] - (int)tok0;
+    const int nqg = (S_b + kRowsPerWG - 1) / kRowsPerWG;
+    const int item = (int)((long long)p.H * nqg * xcd / kXcds) + local;
+    h = item / nqg;
+    qg = item % nqg;
   }
   if (qg * kRowsPerWG >= S_b) return;   // whole workgroup past the end of its sequence
 
@@ -785,14 +849,10 @@ void ssa_fwd_kernel(const Params p) {
   }
 
   // ---- epilogue: O / l in bf16, LSE = r + ln l, skipped-tile count ----
-  long long T = 0, qb_total = 0, qb_off = 0;
+  long long T = 0, qb_off = 0, qb_total = 0;
   if (p.cu_seqlens != nullptr) {
     T = p.cu_seqlens[p.nseq];
-    for (int i = 0; i < p.nseq; ++i) {
-      const long long n = ((long long)p.cu_seqlens[i + 1] - p.cu_seqlens[i] + kBQ - 1) / kBQ;
-      if (i < b) qb_off += n;
-      qb_total += n;
-    }
+    varlen_qblocks(p, b, lane, qb_off, qb_total);
   }
   uint16_t* __restrict__ op = p.o + base;
   const long long ts = p.tok_stride;
@@ -1318,7 +1378,12 @@ int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
     p.lambda_per_seq = 1;
     p.factor = mode == SSA_MODE_FACTOR ? p0 : p0 * std::exp(p1 * p2);
   }
-  const dim3 grid(p.qgroups, H, nseq);
+  // 8 XCD lists, each long enough for an eighth (rounded up) of every
+  // sequence's H * qgroups items.
+  const long long per_xcd = (long long)nseq * (((long long)H * p.qgroups + kXcds - 1) / kXcds);
+  if (per_xcd * kXcds >= (1LL << 31))
+    return fail(SSA_ERR_UNSUPPORTED, "more than 2^31 workgroups (nseq x H x ceil(max_seqlen / %d))", kRowsPerWG);
+  const dim3 grid((unsigned)(per_xcd * kXcds));
   return launch<false>(p, grid, static_cast<hipStream_t>(stream));
 }
 

@@ -57,5 +57,13 @@ def test_bench_json_line():
     roof = d["roofline"]
     assert roof["bound"] in ("hbm", "mfma", "alu") and roof["unit"] in ("GB/s", "TFLOP/s")
     assert roof["peak"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    oc = d["other_configs"]
+    for key in ("wan_like_skip_0.5", "wan_like_skip_0.9", "long_seq_threshold_1e-3", "varlen_calibrated_0.5",
+                "varlen_calibrated_0.7", "varlen_calibrated_0.9"):
+        assert oc[key]["dense_ms"] > 0 and oc[key]["skip_ms"] > 0, key
+        assert 0.0 <= oc[key]["skip_fraction"] <= 1.0, key
+    # more skipping, less time (well separated fractions)
+    assert oc["wan_like_skip_0.9"]["skip_ms"] < d["skip_step"]["ms_mean"] < oc["wan_like_skip_0.5"]["skip_ms"]
+    assert len(oc["varlen_calibrated_0.9"]["skip_fraction_per_sequence"]) == 3
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]

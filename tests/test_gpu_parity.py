@@ -88,6 +88,28 @@ def test_tiny_dense_matches_dense_oracle(ssa):
     assert int(cnt.sum()) == 0
 
 
+@pytest.mark.parametrize("S", [128, 4999])
+def test_dense_instance_equals_general_instance(ssa, S):
+    """Without the skip test the product entry launches the kernel instance
+    whose copies are scheduled for dense work; the debug entry always runs the
+    general instance.  Same arithmetic in the same order: outputs bitwise
+    equal, here over 2 x 5 heads, 40 key tiles and a ragged tail (S = 4999),
+    and at exactly one tile (S = 128)."""
+    w = inputs.random_qkv(61, 2, 5, S)
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    print(f"[case] dense instance S={S}", flush=True)
+    o, lse, cnt = ssa.fwd(q, k, v, scale=w.scale, factor=0.0)
+    od, lsed, cntd, mask, _ = ssa.fwd_debug(q, k, v, scale=w.scale, factor=0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, od) and torch.equal(lse, lsed)
+    assert int(cnt.sum()) == 0 and int(cntd.sum()) == 0 and not bool(mask.any())
+    # and one sampled head against the float64 dense oracle
+    od64, lse64 = oracle.dense_attention(*(oracle.from_bf16(t[1:, 4:]) for t in (w.q, w.k, w.v)), w.scale)
+    err = np.abs(o[1:, 4:].float().cpu().numpy() - od64)
+    assert err.max() <= parity.O_MAX and err.mean() <= parity.O_MEAN
+    assert np.abs(lse[1:, 4:].cpu().numpy() - lse64).max() <= parity.LSE_MAX
+
+
 # ---- planted dominant key: every tile after the first is skipped -----------------
 def _planted(seed=22, S=640, B=1, H=2):
     rng = np.random.default_rng(seed)
@@ -248,6 +270,43 @@ def test_varlen_with_empty_sequence(ssa):
                                                    w.cu_seqlens.tolist(), w.scale, [0.0, 0.0, 0.0])
     assert np.abs(o.float().cpu().numpy() - od).max() <= parity.O_MAX
     assert np.abs(lse.cpu().numpy() - lsed).max() <= parity.LSE_MAX
+
+
+@pytest.mark.parametrize("threshold", [0.0, 0.3])
+def test_varlen_many_sequences_equal_fixed_calls(ssa, threshold):
+    """70 packed sequences (more than one 64-sequence step of the workgroup
+    map's scan) of lengths 0 .. 600, empty, one-token and tile-edge lengths
+    included, with max_seqlen above the longest: each sequence's output,
+    LSE and skip counts equal bitwise those of a fixed-length call on that
+    sequence alone (the same rows, tiles and arithmetic; threshold mode gives
+    both calls the same ln(lambda)).  Checks that the map covers every
+    (sequence, head, query group) once and places it right."""
+    rng = np.random.default_rng(71)
+    lens = [0, 1, 64, 128, 255, 256, 257, 0] + [int(x) for x in rng.integers(0, 601, 62)]
+    H, D = 2, 128
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = (torch.from_numpy(g * rng.standard_normal((T, H, D), dtype=np.float32)).to(torch.bfloat16).cuda()
+               for g in (2.0, 2.0, 1.0))
+    print(f"[case] varlen 70 sequences T={T} threshold={threshold}", flush=True)
+    o, lse, cnt = ssa.fwd_varlen(q, k, v, torch.from_numpy(cu).cuda(), max(lens) + 37, threshold=threshold)
+    torch.cuda.synchronize()
+    qb_off = 0
+    for b, n in enumerate(lens):
+        nqb = -(-n // 64)
+        if n == 0:
+            continue
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        qs, ks, vs = (t[r0:r1].transpose(0, 1).unsqueeze(0).contiguous() for t in (q, k, v))
+        of, lf, cf = ssa.fwd(qs, ks, vs, threshold=threshold)
+        torch.cuda.synchronize()
+        assert torch.equal(o[r0:r1], of[0].transpose(0, 1)), f"sequence {b} (length {n}): output"
+        assert torch.equal(lse[:, r0:r1], lf[0]), f"sequence {b}: lse"
+        assert torch.equal(cnt[:, qb_off:qb_off + nqb], cf[0]), f"sequence {b}: skip counts"
+        qb_off += nqb
+    assert qb_off == cnt.shape[1]
+    if threshold > 0:
+        assert int(cnt.sum()) > 0
 
 
 def test_errors_on_gpu(ssa):
