@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -165,10 +165,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[fl
 def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                max_seqlen: int, *, scale: Optional[float] = None, factor: Optional[float] = None,
                threshold: Optional[float] = None, calib=None, with_lse: bool = True,
-               with_counts: bool = True):
+               with_counts: bool = True, seqlens: Optional[Sequence[int]] = None):
     """Packed variable-length batch: q, k, v bf16 [T, H, 128], cu_seqlens int32
     [nseq + 1] on the device.  Each sequence normalises lambda by its own
-    length.  Returns (o [T, H, 128], lse [H, T], skip_counts [H, sum ceil(S_b/64)])."""
+    length.  Returns (o [T, H, 128], lse [H, T], skip_counts [H, sum ceil(S_b/64)]).
+    The skip counts' size comes from the sequence lengths: pass them on the
+    host as ``seqlens`` to avoid reading cu_seqlens back from the device
+    (a synchronisation that HIP graph capture does not allow)."""
     _check_qkv(q, k, v, 3)
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be an int32 1-D tensor on the same device as q")
@@ -176,7 +179,14 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     mode, p0, p1, p2 = _control(factor, threshold, calib)
     nseq = cu_seqlens.numel() - 1
-    lens = (cu_seqlens[1:] - cu_seqlens[:-1]).tolist() if with_counts else []
+    if not with_counts:
+        lens = []
+    elif seqlens is not None:
+        lens = [int(n) for n in seqlens]
+        if len(lens) != nseq:
+            raise ValueError(f"seqlens has {len(lens)} entries for {nseq} sequences")
+    else:
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).tolist()
     o = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if with_lse else None
     cnt = None
