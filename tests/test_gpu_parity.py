@@ -272,7 +272,7 @@ def test_varlen_with_empty_sequence(ssa):
     assert np.abs(lse.cpu().numpy() - lsed).max() <= parity.LSE_MAX
 
 
-@pytest.mark.parametrize("threshold", [0.0, 0.3])
+@pytest.mark.parametrize("threshold", [0.0, 0.3, 2.0])
 def test_varlen_many_sequences_equal_fixed_calls(ssa, threshold):
     """70 packed sequences (more than one 64-sequence step of the workgroup
     map's scan) of lengths 0 .. 600, empty, one-token and tile-edge lengths
@@ -280,7 +280,8 @@ def test_varlen_many_sequences_equal_fixed_calls(ssa, threshold):
     LSE and skip counts equal bitwise those of a fixed-length call on that
     sequence alone (the same rows, tiles and arithmetic; threshold mode gives
     both calls the same ln(lambda)).  Checks that the map covers every
-    (sequence, head, query group) once and places it right."""
+    (sequence, head, query group) once and places it right; lambda = 2
+    adds the cascade of decisions that kept tiles cause above 1."""
     rng = np.random.default_rng(71)
     lens = [0, 1, 64, 128, 255, 256, 257, 0] + [int(x) for x in rng.integers(0, 601, 62)]
     H, D = 2, 128
