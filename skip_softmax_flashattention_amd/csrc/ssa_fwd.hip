@@ -8,7 +8,8 @@
 // Work decomposition.  One workgroup = 8 waves = 256 query rows of one
 // (sequence, head); each wave owns 32 rows, and the two waves 2g, 2g+1 form
 // the 64-row vote group g of the skip test.  Workgroups are renumbered so
-// that each XCD works through whole heads, sharing K/V tiles in its L2.
+// that each XCD works through whole heads, sharing K/V tiles in its L2; in a
+// packed batch each XCD takes an eighth of every sequence's work.
 // Key tiles of 128 keys stream through LDS (K and V double buffered, shared
 // by all eight waves), copied from global memory straight into LDS by
 // buffer loads with the LDS-destination bit; keys past the end of the
@@ -178,8 +179,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
 }
 
-// Packed batches: the number of items sequence sb contributes (0 for a
-// length that is negative or above max_seqlen, or past the last sequence).
+// Packed batches: the length of sequence sb as the work map counts it (0
+// for a length that is negative or above max_seqlen, and past the last
+// sequence).
 __device__ __forceinline__ int varlen_len(const Params& p, int sb) {
   int len = sb < p.nseq ? p.cu_seqlens[sb + 1] - p.cu_seqlens[sb] : 0;
   return (len < 0 || len > p.S) ? 0 : len;
