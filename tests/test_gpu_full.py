@@ -5,7 +5,9 @@ checks every output that is cheap to check and samples the rest:
   * determinism and product/debug agreement over the whole problem;
   * skip_counts equal to the debug mask's row sums everywhere;
   * tile mask, O and LSE against the oracle on seeded samples of query blocks
-    (rows are independent given K and V, so a sampled block is exact);
+    (rows are independent given K and V, so a sampled block is exact); for
+    the long sequence and the varlen batch against both oracles (float64
+    numpy and the single-precision C recurrence);
   * lambda = 0 skips nothing.
 """
 import json
@@ -16,6 +18,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import c_oracle
 from skip_softmax_flashattention_amd import inputs
 from tests import parity
 
@@ -51,7 +54,7 @@ def _whole_problem_checks(ssa, q, k, v, scale, **kw):
     return o1, l1, c1, mask.cpu().numpy().astype(bool)
 
 
-def _sampled(w, ln, o, lse, cnt, mask, heads, per_head, seed):
+def _sampled(w, ln, o, lse, cnt, mask, heads, per_head, seed, ref=None):
     rng = np.random.default_rng(seed)
     B, H, S, D = w.q.shape
     nqb = -(-S // 64)
@@ -65,7 +68,7 @@ def _sampled(w, ln, o, lse, cnt, mask, heads, per_head, seed):
         rows = rows[rows < S]
         qd, kd, vd = (oracle.from_bf16(t[0, h]) for t in (w.q, w.k, w.v))
         reports.append(parity.compare_head_blocks(qd, kd, vd, w.scale, ln, qbs, mask[0, h][qbs], o_np[0, h][rows],
-                                                  lse_np[0, h][rows], cnt_np[0, h][qbs]))
+                                                  lse_np[0, h][rows], cnt_np[0, h][qbs], ref=ref))
     return parity.merge(reports)
 
 
@@ -102,6 +105,10 @@ def test_long_sequence(ssa):
         rep = _sampled(w, ln, o, lse, cnt, mask, heads=(0, 23), per_head=6, seed=3)
         print(f"[case] long {lam}: whole-problem skip fraction {mask.mean():.4f}; sampled {rep}", flush=True)
         parity.assert_bar(rep)
+        # the same samples against the single-precision C oracle
+        rep_c = _sampled(w, ln, o, lse, cnt, mask, heads=(0, 23), per_head=6, seed=3, ref=c_oracle.oracle().skip_head)
+        print(f"[case] long {lam}: fp32 C oracle {rep_c}", flush=True)
+        parity.assert_bar(rep_c)
 
 
 @pytest.fixture(scope="module")
@@ -148,6 +155,8 @@ def test_calibrated_varlen(ssa, varlen_batch, target):
         ln = oracle.ln_lambda_f32(oracle.resolve_lambda(a=a, b=b, target_sparsity=target, seqlen=n))
         seq_w = inputs.Workload("seq", qs, ks, vs, scale=w.scale)
         reports.append(_sampled(seq_w, ln, od, ld, cd, mask_np, heads=(0, 15), per_head=4, seed=100 + bi))
+        reports.append(_sampled(seq_w, ln, od, ld, cd, mask_np, heads=(0, 15), per_head=4, seed=100 + bi,
+                                ref=c_oracle.oracle().skip_head))
         off += nqb
     rep = parity.merge(reports)
     print(f"[case] calibrated varlen target {target}: achieved skip fraction per sequence "
