@@ -5,9 +5,9 @@ checks every output that is cheap to check and samples the rest:
   * determinism and product/debug agreement over the whole problem;
   * skip_counts equal to the debug mask's row sums everywhere;
   * tile mask, O and LSE against the oracle on seeded samples of query blocks
-    (rows are independent given K and V, so a sampled block is exact); for
-    the long sequence and the varlen batch against both oracles (float64
-    numpy and the single-precision C recurrence);
+    (rows are independent given K and V, so a sampled block is exact),
+    against both oracles (float64 numpy and the single-precision C
+    recurrence);
   * lambda = 0 skips nothing.
 """
 import json
@@ -88,6 +88,10 @@ def test_wan_like(ssa, wan, frac):
     rep = _sampled(wan, ln, o, lse, cnt, mask, heads=(0, 17, 39), per_head=6, seed=int(float(frac) * 100))
     print(f"[case] wan-like {frac}: whole-problem skip fraction {mask.mean():.4f}; sampled {rep}", flush=True)
     parity.assert_bar(rep)
+    rep_c = _sampled(wan, ln, o, lse, cnt, mask, heads=(0, 17, 39), per_head=6, seed=int(float(frac) * 100),
+                     ref=c_oracle.oracle().skip_head)
+    print(f"[case] wan-like {frac}: fp32 C oracle {rep_c}", flush=True)
+    parity.assert_bar(rep_c)
     if frac == "0":
         assert not mask.any()
     else:
