@@ -116,3 +116,43 @@ def test_graph_virtual_and_fp8(ssa, grid_w):
     torch.cuda.synchronize()
     _replays_match(g, list(out_v) + list(out_8) + list(g8), list(ref_v) + list(ref_8) + list(ref_q),
                    lambda: ssa.fwd(q, k, v, threshold=0.05, scale=grid_w.scale))
+
+
+def test_two_host_threads_two_streams(ssa, grid_w):
+    """Two host threads, each on its own stream, call the library at the same
+    time (ctypes releases the GIL during the call): one the fixed-length skip
+    call, the other the packed entry.  Every result equals the serial one."""
+    import threading
+    q, k, v = (t.cuda() for t in (grid_w.q, grid_w.k, grid_w.v))
+    wv = inputs.varlen(seed=43, heads=2, grids=((1, 7, 10), (3, 10, 13)))
+    qv, kv, vv = (t.cuda() for t in (wv.q, wv.k, wv.v))
+    cu = wv.cu_seqlens.cuda()
+    ref_a = ssa.fwd(q, k, v, threshold=0.3, scale=grid_w.scale)
+    ref_b = ssa.fwd_varlen(qv, kv, vv, cu, max(wv.seqlens), factor=2.0, scale=wv.scale)
+    torch.cuda.synchronize()
+    outs, errors = {"a": [], "b": []}, []
+
+    def run(name, fn):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(8):
+                    outs[name].append(fn())
+            s.synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    ta = threading.Thread(target=run, args=("a", lambda: ssa.fwd(q, k, v, threshold=0.3, scale=grid_w.scale)))
+    tb = threading.Thread(target=run, args=("b", lambda: ssa.fwd_varlen(qv, kv, vv, cu, max(wv.seqlens), factor=2.0,
+                                                                        scale=wv.scale, seqlens=wv.seqlens)))
+    ta.start()
+    tb.start()
+    ta.join()
+    tb.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for got in outs["a"]:
+        assert all(torch.equal(x, y) for x, y in zip(got, ref_a))
+    for got in outs["b"]:
+        assert all(torch.equal(x, y) for x, y in zip(got, ref_b))
+    assert len(outs["a"]) == len(outs["b"]) == 8
