@@ -20,6 +20,7 @@ at target sparsity 0.5, 0.7 and 0.9), each paired with its own lambda = 0
 call; and the CPU oracle timed on a bounded sample as a baseline only.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15]
+    python bench.py --power 200      # socket power and energy per call instead
 """
 from __future__ import annotations
 
@@ -120,6 +121,55 @@ def copy_reference(launches):
     print(json.dumps({"counters_run": "copy", "bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}), flush=True)
 
 
+def power_run(ssa, q, k, v, scale, factor, calls):
+    """Socket power while the dense and the skip calls each run back to back.
+
+    Reads the GPU's hwmon power1_input (and power1_cap) every 20 ms from a
+    host thread; nothing is written.  Returns a dict, or None where the
+    files cannot be read."""
+    import glob
+    import threading
+    import numpy as np
+    import torch
+    files = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+    if not files:
+        return None
+
+    def read(path):
+        with open(path) as f:
+            return float(f.read())
+    try:
+        cap = read(files[0].replace("power1_input", "power1_cap")) / 1e6
+    except OSError:
+        cap = None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append((time.time(), read(files[0]) / 1e6))
+            time.sleep(0.02)
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(1.0)
+    out = {"cap_w": cap, "idle_w": round(float(np.mean([w for _, w in samples])), 1)}
+    for name, f in (("dense", 0.0), ("skip", factor)):
+        for _ in range(10):
+            ssa.fwd(q, k, v, factor=f, scale=scale)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for _ in range(calls):
+            ssa.fwd(q, k, v, factor=f, scale=scale)
+        torch.cuda.synchronize()
+        t1 = time.time()
+        ms = (t1 - t0) / calls * 1e3
+        settle = min(0.5, 0.3 * (t1 - t0))   # leave out the start of the run, where power still rises
+        watts = float(np.mean([w for t, w in samples if t0 + settle <= t <= t1]))
+        out[name] = {"ms_per_call": round(ms, 3), "power_w": round(watts, 1), "energy_j_per_call": round(watts * ms / 1e3, 2)}
+    stop.set()
+    th.join()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +178,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--target", type=float, default=0.75, help="skip fraction of the timed step")
+    ap.add_argument("--power", type=int, default=0, metavar="CALLS",
+                    help="instead of the benchmark: socket power (hwmon, read-only) over CALLS back-to-back dense "
+                         "and then skip calls")
     ap.add_argument("--counters", choices=("dense", "skip", "copy"), default=None,
                     help="launch only one configuration (or the plain copy reference), for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -157,6 +210,12 @@ def main():
     B, H, S, D = q.shape
     factor = lam * S
     dense_flops = 4.0 * B * H * S * S * D
+
+    if args.power > 0:
+        print(json.dumps({"power_run": power_run(ssa, q, k, v, w.scale, factor, args.power),
+                          "workload": "wan-like B=1 H=40 S=32760 D=128", "lambda": lam,
+                          "kernel_sha256_16": kernel_hash()}), flush=True)
+        return
 
     if args.counters is not None:
         # Only the requested configuration: warmup + steps launches of one kernel.

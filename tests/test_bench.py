@@ -67,3 +67,20 @@ def test_bench_json_line():
     assert len(oc["varlen_calibrated_0.9"]["skip_fraction_per_sequence"]) == 3
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+
+
+@pytest.mark.gpu
+def test_bench_power_mode():
+    """--power prints one JSON line with the cap, idle power and, for the dense
+    and skip calls, time, power and energy per call (read-only hwmon)."""
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--power", "30"],
+                       capture_output=True, text=True, timeout=280, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])["power_run"]
+    if d is None:
+        pytest.skip("no readable hwmon power file on this machine")
+    for name in ("dense", "skip"):
+        e = d[name]
+        assert e["ms_per_call"] > 0 and e["power_w"] > 0
+        assert abs(e["energy_j_per_call"] - e["power_w"] * e["ms_per_call"] / 1e3) < 0.01
+    assert d["skip"]["ms_per_call"] < d["dense"]["ms_per_call"]
