@@ -90,6 +90,9 @@ class COracle:
         self.lib.oracle_skip_head_f32.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_float, _I, ctypes.c_float, _I, _I,
                                                   _P, _I, _P, _P, _P, _P, _P]
         self.lib.oracle_skip_head_f32.restype = _I
+        self.lib.oracle_skip_mask_f32.argtypes = [_P, _P, _I, _I, ctypes.c_float, _I, ctypes.c_float, _I, _I, _P, _I,
+                                                  _P, _P]
+        self.lib.oracle_skip_mask_f32.restype = _I
 
     def threads(self) -> int:
         return int(self.lib.oracle_threads())
@@ -144,6 +147,28 @@ class COracle:
         if rc != 0:
             raise MemoryError("oracle_skip_head_f32: out of memory")
         return HeadResult(o=o, lse=lse, skipped=skipped.astype(bool), margin=margin, qblocks=qb)
+
+    def skip_mask(self, q: np.ndarray, k: np.ndarray, scale: float, ln_lambda: Optional[np.float32],
+                  qblocks: Optional[Iterable[int]] = None, block_q: int = BLOCK_Q, block_k: int = BLOCK_K):
+        """The tile decisions and margins of the single-precision recurrence
+        alone (scores, tile maxima, vote, running maximum of the kept tiles;
+        no exponentials and no P.V).  Returns (skipped [nb, nKT] bool,
+        margin [nb, nKT] float32), equal to skip_head's."""
+        q, k = (np.ascontiguousarray(x, dtype=np.float32) for x in (q, k))
+        S, D = q.shape
+        nqb, nkt = -(-S // block_q), -(-S // block_k)
+        qb = np.arange(nqb, dtype=np.int64) if qblocks is None else np.ascontiguousarray(list(qblocks), dtype=np.int64)
+        nb = len(qb)
+        skipped = np.empty((nb, nkt), np.uint8)
+        margin = np.empty((nb, nkt), np.float32)
+        vote = ln_lambda is not None
+        rc = self.lib.oracle_skip_mask_f32(
+            q.ctypes.data, k.ctypes.data, S, D, float(np.float32(scale)), int(vote),
+            float(np.float32(ln_lambda)) if vote else 0.0, block_q, block_k, qb.ctypes.data, nb,
+            skipped.ctypes.data, margin.ctypes.data)
+        if rc != 0:
+            raise MemoryError("oracle_skip_mask_f32: out of memory")
+        return skipped.astype(bool), margin
 
     def skip_attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                        ln_lambda: Optional[np.float32], forced_skip: Optional[np.ndarray] = None,

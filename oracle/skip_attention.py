@@ -338,8 +338,10 @@ def lambda_for_skip_fraction(margins: np.ndarray, fraction: float) -> float:
     a tile.  Returns 0.0 for fraction 0.  Raises if the fraction needs
     lambda > 1 (where the closed form no longer holds).
 
-    Parity unpinned beyond the closed form it inverts: it chooses a workload
-    parameter, it does not compute a result of the method.
+    Pinned against brute force over every candidate threshold (the float32
+    values just above the margins), ties, first tiles and margins >= 0
+    included.  It chooses a workload parameter; it computes no result of the
+    method.
     """
     flat = np.sort(margins.reshape(-1).astype(np.float64))
     if fraction <= 0.0:

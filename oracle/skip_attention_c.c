@@ -14,6 +14,9 @@
  *                         vLLM-Omni, section "Algorithm"; "Skip-Softmax" page
  *                         of the vLLM-Omni documentation, sections "The
  *                         online-softmax pass" and "The skip test").
+ *   oracle_skip_mask_f32  the same recurrence reduced to what the tile
+ *                         decisions depend on (scores, tile maxima, the vote
+ *                         and the running maximum of the kept tiles).
  *
  * Readings taken where the pages leave a step open (the same ones the
  * Python oracle takes): the running maximum is the one held before the tile
@@ -107,9 +110,10 @@ int oracle_dense_head(const double* q, const double* k, const double* v, int S, 
  * meaningless), skipped [nb][nkt], margin [nb][nkt] = max over valid rows of
  * tile_max - m (+inf on a block's first tile).  Returns 0, or -1 when scratch
  * memory is missing. */
-int oracle_skip_head_f32(const float* q, const float* k, const float* v, int S, int D, int Dv, float scale, int vote,
+static int skip_head_f32(const float* q, const float* k, const float* v, int S, int D, int Dv, float scale, int vote,
                          float ln_lambda, int block_q, int block_k, const int64_t* qblocks, int nb,
-                         const uint8_t* forced, float* o, float* lse, uint8_t* skipped, float* margin) {
+                         const uint8_t* forced, int mask_only, float* o, float* lse, uint8_t* skipped,
+                         float* margin) {
   const int nkt = (S + block_k - 1) / block_k;
   int failed = 0;
 #pragma omp parallel
@@ -125,12 +129,12 @@ int oracle_skip_head_f32(const float* q, const float* k, const float* v, int S, 
 #pragma omp for schedule(dynamic, 1)
       for (int b = 0; b < nb; ++b) {
         const int r0 = (int)qblocks[b] * block_q;
-        float* ob = o + (size_t)b * block_q * Dv;
+        float* ob = mask_only ? NULL : o + (size_t)b * block_q * Dv;
         for (int i = 0; i < block_q; ++i) {
           m[i] = -INFINITY;
           l[i] = 0.f;
         }
-        memset(ob, 0, sizeof(float) * (size_t)block_q * Dv);
+        if (!mask_only) memset(ob, 0, sizeof(float) * (size_t)block_q * Dv);
         for (int kt = 0; kt < nkt; ++kt) {
           const int c0 = kt * block_k;
           const int c1 = (c0 + block_k < S) ? c0 + block_k : S;
@@ -190,9 +194,14 @@ int oracle_skip_head_f32(const float* q, const float* k, const float* v, int S, 
 #endif
             continue;   /* 4. a skipped tile leaves m, l and O untouched */
           }
-          /* 5. a kept tile is absorbed exactly */
+          /* 5. a kept tile is absorbed exactly (only its maximum when just the
+           * decisions are wanted: l and O never feed back into them) */
           for (int i = 0; i < block_q; ++i) {
             const float mn = tmax[i] > m[i] ? tmax[i] : m[i];
+            if (mask_only) {
+              m[i] = mn;
+              continue;
+            }
 #if ORACLE_MUTANT == 3
             const float alpha = 1.f;   /* l and O not rescaled */
 #else
@@ -210,7 +219,7 @@ int oracle_skip_head_f32(const float* q, const float* k, const float* v, int S, 
             m[i] = mn;
           }
         }
-        for (int i = 0; i < block_q; ++i) {
+        for (int i = 0; i < block_q && !mask_only; ++i) {
           float* oi = ob + (size_t)i * Dv;
           for (int t = 0; t < Dv; ++t) oi[t] /= l[i];
 #if ORACLE_MUTANT == 7
@@ -227,4 +236,22 @@ int oracle_skip_head_f32(const float* q, const float* k, const float* v, int S, 
     free(tmax);
   }
   return failed ? -1 : 0;
+}
+
+int oracle_skip_head_f32(const float* q, const float* k, const float* v, int S, int D, int Dv, float scale, int vote,
+                         float ln_lambda, int block_q, int block_k, const int64_t* qblocks, int nb,
+                         const uint8_t* forced, float* o, float* lse, uint8_t* skipped, float* margin) {
+  return skip_head_f32(q, k, v, S, D, Dv, scale, vote, ln_lambda, block_q, block_k, qblocks, nb, forced, 0, o, lse,
+                       skipped, margin);
+}
+
+/* The same recurrence for the tile decisions and margins alone: the scores,
+ * each row's tile maximum, the vote, and for a kept tile the running maximum
+ * m' = max(m, tile_max).  The decisions depend on nothing else (l and O never
+ * enter the test), so they equal oracle_skip_head_f32's, at about half the
+ * work (no exponentials, no P.V).  v, o and lse are not used. */
+int oracle_skip_mask_f32(const float* q, const float* k, int S, int D, float scale, int vote, float ln_lambda,
+                         int block_q, int block_k, const int64_t* qblocks, int nb, uint8_t* skipped, float* margin) {
+  return skip_head_f32(q, k, NULL, S, D, 0, scale, vote, ln_lambda, block_q, block_k, qblocks, nb, NULL, 1, NULL, NULL,
+                       skipped, margin);
 }

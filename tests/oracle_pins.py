@@ -497,4 +497,42 @@ def pin_virtual_tiles_between_skip_and_dense(orc):
     assert (lv > lse_skip + 1e-9).mean() > 0.5      # the virtual keys do add weight
 
 
+def pin_lambda_for_skip_fraction_bruteforce(orc):
+    """lambda_for_skip_fraction(margins, f) returns the smallest lambda <= 1
+    whose mask margin < ln(lambda) (ln taken as the library takes it: the
+    float64 log rounded to float32) skips at least a fraction f of the tiles.
+    Brute force: every float32 just above a distinct negative margin is a
+    candidate ln(lambda) (the mask only changes there); the answer is the
+    smallest candidate that reaches f.  Margins include ties, first tiles
+    (+inf) and values at and above 0; a fraction that needs lambda > 1 is
+    refused."""
+    rng = np.random.default_rng(31)
+    m = (rng.standard_normal((20, 13)) * 2.0 - 3.0).astype(np.float32)
+    m[:, 0] = np.inf                       # first tiles are never skipped
+    m[3, 4:9] = m[2, 5]                    # ties
+    m[5, 2] = 0.0
+    m[6, 3] = np.float32(0.75)
+    cands = sorted({float(np.nextafter(x, np.float32(np.inf))) for x in m.reshape(-1)
+                    if np.isfinite(x) and x < 0})
+    for frac in (0.0, 1e-3, 0.05, 0.1, 0.37, 0.5, 0.75, 0.85):
+        lam = orc.lambda_for_skip_fraction(m, frac)
+        if frac == 0.0:
+            assert lam == 0.0
+            continue
+        assert 0.0 < lam < 1.0
+        ln = orc.ln_lambda_f32(lam)
+        got = float((m < ln).mean())
+        assert got >= frac, (frac, got)
+        best = next(t for t in cands if float((m < np.float32(t)).mean()) >= frac)
+        assert float(ln) == best, (frac, float(ln), best)
+    reach = float((m < 0).mean())          # the most lambda <= 1 can skip
+    for frac in (reach + 0.01, 0.99):
+        try:
+            orc.lambda_for_skip_fraction(m, frac)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"fraction {frac} needs lambda > 1 and was not refused")
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

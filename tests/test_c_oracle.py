@@ -252,10 +252,65 @@ def pin_padding_rows_do_not_vote(c):
     assert r.skipped[4, 1:].all()
 
 
+def pin_mask_only_mode(c):
+    """The decisions-only entry (no exponentials, no P.V) against the same
+    pins the full recurrence's decisions meet: the closed form by brute force
+    (lambda <= 1, ragged), the strict tie, the running maximum before the
+    update, padding rows that do not vote, and a three-tile cascade
+    (lambda = e^2) in which a skipped tile must not raise m: tile 1 raises
+    every row's maximum by 0.5 and is skipped, tile 2 by 2.3 over tile 0 and
+    must be kept (1.8 over tile 1).  It also equals the full recurrence's
+    decisions and margins on a peaked head at lambda below and above 1."""
+    for seed, S, D, bq, bk, scale in ((13, 40, 4, 4, 8, 0.5), (14, 37, 3, 5, 7, 0.6)):
+        q, k, v = _peaky_head(seed, S, D)
+        want = _bruteforce_margins(q.tolist(), k.tolist(), scale, bq, bk)
+        for lam in (1e-3, 0.05, 0.5, 1.0):
+            ln = ln_lambda_f32(lam)
+            sk, mg = c.skip_mask(q, k, scale, ln, block_q=bq, block_k=bk)
+            fin = np.isfinite(want)
+            assert np.abs(mg[fin] - want[fin]).max() < BAND and (np.isinf(mg) == ~fin).all()
+            clear = np.abs(want - float(ln)) > BAND
+            assert (sk[clear] == (want < float(ln))[clear]).all(), lam
+            full = c.skip_head(q, k, v, scale, ln, block_q=bq, block_k=bk)
+            assert np.array_equal(sk, full.skipped) and np.array_equal(mg, full.margin)
+    # strict tie
+    S = 256
+    q = np.ones((S, 1))
+    k = np.full((S, 1), -10.0)
+    k[0] = 0.0
+    k[128:] = -3.0
+    k[200] = -2.0
+    sk, mg = c.skip_mask(q, k, 1.0, ln_lambda_f32(math.exp(-2.0)))
+    assert (mg[:, 1] == np.float32(-2.0)).all() and not sk.any()
+    sk, _ = c.skip_mask(q, k, 1.0, np.nextafter(np.float32(-2.0), np.float32(0.0)))
+    assert sk[:, 1].all() and not sk[:, 0].any()
+    # cascade: a skipped tile leaves m alone, so a later tile is measured against tile 0
+    k = np.full((384, 1), -20.0)
+    k[3], k[130], k[260] = 0.0, 0.5, 2.3
+    sk, mg = c.skip_mask(np.ones((384, 1)), k, 1.0, ln_lambda_f32(math.exp(2.0)))
+    assert np.isinf(mg[:, 0]).all() and not sk[:, 0].any()
+    assert sk[:, 1].all() and (mg[:, 1] == np.float32(0.5)).all()
+    assert not sk[:, 2].any() and (mg[:, 2] == np.float32(2.3)).all()
+    # padding rows do not vote
+    rng = np.random.default_rng(25)
+    q = _bf(-np.abs(rng.standard_normal((260, 8))))
+    k = _bf(np.abs(rng.standard_normal((260, 8))))
+    k[3] = _bf(np.full(8, -6.0))
+    sk, _ = c.skip_mask(q, k, 1.0, ln_lambda_f32(1e-2))
+    assert sk.shape == (5, 3) and sk[4, 1:].all()
+    # equal to the full recurrence, lambda below and above 1
+    q, k, v = _peaky_head(26, 700, 16, gain=4.0)
+    for lam in (1e-3, 0.3, 3.0, 50.0):
+        ln = ln_lambda_f32(lam)
+        sk, mg = c.skip_mask(q, k, 0.4, ln, block_q=64, block_k=128)
+        full = c.skip_head(q, k, v, 0.4, ln, block_q=64, block_k=128)
+        assert np.array_equal(sk, full.skipped) and np.array_equal(mg, full.margin), lam
+
+
 PINS = [pin_dense_matches_torch_sdpa, pin_dense_bruteforce, pin_zero_threshold_is_dense,
         pin_mask_matches_bruteforce, pin_output_is_masked_softmax, pin_skipped_weight_bound,
         pin_omitted_mass, pin_strict_tie_keeps_tile, pin_running_max_before_update,
-        pin_planted_dominant_key, pin_padding_rows_do_not_vote]
+        pin_planted_dominant_key, pin_padding_rows_do_not_vote, pin_mask_only_mode]
 
 
 @pytest.fixture(scope="module")

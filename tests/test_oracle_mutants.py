@@ -76,6 +76,12 @@ MUTANTS = [
      "counts = np.array([block_k for t in range(nkt)], dtype=np.float64)"),
     ("virtual keys double-count kept keys",
      "kept = ~sk[key_tile]", "kept = np.ones(S, dtype=bool)"),
+    ("lambda for a fraction one step too low",
+     "ln_lam = float(np.nextafter(np.float32(edge), np.float32(np.inf)))", "ln_lam = float(np.float32(edge))"),
+    ("lambda for a fraction with the count rounded down",
+     "need = int(math.ceil(fraction * n))", "need = max(1, int(math.floor(fraction * n)))"),
+    ("lambda for a fraction off by one tile",
+     "edge = flat[need - 1]", "edge = flat[min(need, n - 1)]"),
 ]
 
 
