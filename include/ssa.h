@@ -38,7 +38,12 @@
  *   lse           float [B, H, S]: LSE_i = m_i + ln(l_i), natural log of the
  *                 row's softmax denominator over the kept tiles. May be NULL.
  *   skip_counts   int32 [B, H, ceil(S/64)]: number of skipped key tiles of
- *                 each 64-row query block. May be NULL.
+ *                 each 64-row query block. May be NULL.  The two waves of a
+ *                 block exchange their halves of the vote with a bounded
+ *                 wait (ssa_set_vote_poll_limit); a wave that gives up keeps
+ *                 the tile, which is always exact, and the block's count is
+ *                 then stored as -1 - count, so a negative count flags a
+ *                 block whose decisions may differ between its two halves.
  * Inputs o, lse and skip_counts are overwritten; q, k, v are read only.
  *
  * Errors.  Every argument is checked on the host before any HIP call; a bad
@@ -97,7 +102,12 @@ int ssa_fwd_calibrated(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int S, int D, float scale, float a, float b,
                        float target_sparsity, int seqlen, int32_t* skip_counts, void* stream);
 
-/* Packed variable-length batch ("cu_seqlens" layout): sequence b holds the
+/* Packed variable-length batch ("cu_seqlens" layout of the SGLang SubBlock
+ * sparse-attention article for the MiniMax-H3 video DiT, section on the
+ * varlen path, where a packed batch is split per document by cu_seqlens),
+ * with the threshold normalised by each sequence's own length
+ * ("Skip-Softmax" page of the vLLM-Omni documentation, section "The
+ * threshold"): sequence b holds the
  * tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, k, v, o, which are bf16
  * [T, H, D] with T = cu_seqlens[nseq].  cu_seqlens: device int32 [nseq + 1],
  * non-decreasing from 0; every length must be <= max_seqlen (the kernel
@@ -176,10 +186,14 @@ int ssa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const float* q_scale, cons
                 uint8_t* tile_mask, float* tile_margin, void* stream);
 
 /* Any of the three controls (see ssa_mode; S_b = seqlen) with every tile
- * decision reported: tile_mask uint8 [B, H, ceil(S/64), ceil(S/128)]
- * (1 = skipped) and tile_margin float (same shape, nullable): the largest
+ * decision of the skip test reported ("Skip-Softmax" design document of
+ * vLLM-Omni, section "Algorithm": the per-tile test of every row's tile
+ * maximum against its running maximum, evaluated in log space):
+ * tile_mask uint8 [B, H, ceil(S/64), ceil(S/128)] (1 = skipped, must not be
+ * NULL) and tile_margin float (same shape, nullable): the largest
  * tile_max[i] - m[i] over the block's valid rows, +inf on the first tile.
- * Same arithmetic as the other entry points. */
+ * Same arithmetic as the other entry points, so o, lse and skip_counts equal
+ * theirs bit for bit. */
 int ssa_fwd_debug(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int S, int D, float scale, int mode, double p0, double p1,
                   double p2, int seqlen, int32_t* skip_counts, uint8_t* tile_mask,
@@ -244,6 +258,17 @@ int ssa_flow_shift_schedule(double shift, int num_inference_steps, double* t_out
 
 /* SSA_OK when the current HIP device is gfx950. */
 int ssa_device_check(void);
+
+/* The bound of the wait for the partner's half of the vote, in polls of one
+ * LDS word, for every later call of this process (default 16384).  The two
+ * halves are published in the same phase, so the bound only guards against
+ * a wave that never arrives; a test sets it to 0 to drive the give-up path
+ * from the host (every tile with the test on is then kept and every count
+ * comes out as -1 - count, see skip_counts above).  0 <= polls <= 2^24,
+ * else SSA_ERR_INVALID_ARG.  Host only; not synchronised with calls already
+ * enqueued. */
+int ssa_set_vote_poll_limit(int polls);
+int ssa_vote_poll_limit(void);
 
 const char* ssa_strerror(int status);
 const char* ssa_last_error(void);

@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "SsaError", "fwd", "fwd_varlen", "fwd_debug", "fwd_max_prob", "fwd_virtual", "virtual_workspace_bytes",
-    "quantize_qk_fp8", "fwd_fp8", "resolve_threshold", "device_check",
+    "quantize_qk_fp8", "fwd_fp8", "resolve_threshold", "device_check", "set_vote_poll_limit", "vote_poll_limit",
     "library_path", "load_library", "BLOCK_Q", "BLOCK_K", "HEAD_DIM",
     "MODE_FACTOR", "MODE_THRESHOLD", "MODE_CALIBRATED",
 ]
@@ -38,7 +38,7 @@ MODE_FACTOR, MODE_THRESHOLD, MODE_CALIBRATED = 0, 1, 2
 SSA_OK = 0
 STATUS_NAMES = {
     0: "SSA_OK", -1: "SSA_ERR_INVALID_ARG", -2: "SSA_ERR_UNSUPPORTED", -3: "SSA_ERR_BAD_THRESHOLD",
-    -4: "SSA_ERR_NO_CALIBRATION", -5: "SSA_ERR_DEVICE", -6: "SSA_ERR_LAUNCH",
+    -4: "SSA_ERR_NO_CALIBRATION", -5: "SSA_ERR_DEVICE", -6: "SSA_ERR_LAUNCH", -7: "SSA_ERR_BAD_CONFIG",
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +83,10 @@ def load_library() -> ctypes.CDLL:
                  "ssa_resolve_threshold", "ssa_device_check", "ssa_version"):
         getattr(lib, name).restype = I
     lib.ssa_device_check.argtypes = []
+    lib.ssa_set_vote_poll_limit.argtypes = [I]
+    lib.ssa_set_vote_poll_limit.restype = I
+    lib.ssa_vote_poll_limit.argtypes = []
+    lib.ssa_vote_poll_limit.restype = I
     lib.ssa_version.argtypes = []
     lib.ssa_strerror.argtypes = [I]
     lib.ssa_strerror.restype = ctypes.c_char_p
@@ -132,6 +136,40 @@ def _check_qkv(q, k, v, ndim):
         raise ValueError("q, k and v must be on the same device")
 
 
+def _check_out(out: torch.Tensor, q: torch.Tensor) -> None:
+    """A caller-supplied output must be what the kernel writes: a contiguous
+    bf16 tensor of q's shape on q's device."""
+    if not isinstance(out, torch.Tensor):
+        raise ValueError("out must be a tensor")
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or out.device != q.device \
+            or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {tuple(q.shape)} on {q.device}")
+
+
+def _varlen_lengths(cu_seqlens: torch.Tensor, T: int, max_seqlen: int, seqlens: Optional[Sequence[int]],
+                    read_back: bool) -> Optional[list]:
+    """The sequence lengths of a packed batch on the host: ``seqlens`` when
+    given, else read back from the device cu_seqlens when ``read_back``, else
+    None.  Lengths known on the host are checked against the packed tensors:
+    one per sequence, none negative or above max_seqlen, summing to T."""
+    nseq = cu_seqlens.numel() - 1
+    if seqlens is not None:
+        lens = [int(n) for n in seqlens]
+    elif read_back:
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).tolist()
+    else:
+        return None
+    if len(lens) != nseq:
+        raise ValueError(f"seqlens has {len(lens)} entries for {nseq} sequences")
+    if any(n < 0 for n in lens):
+        raise ValueError("sequence lengths must be non-negative")
+    if lens and max(lens) > max_seqlen:
+        raise ValueError(f"a sequence of {max(lens)} tokens exceeds max_seqlen = {max_seqlen}")
+    if sum(lens) != T:
+        raise ValueError(f"the sequence lengths sum to {sum(lens)}, but q holds {T} tokens")
+    return lens
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
         factor: Optional[float] = None, threshold: Optional[float] = None, calib=None,
         seqlen: Optional[int] = None, with_lse: bool = True, with_counts: bool = True,
@@ -140,9 +178,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[fl
 
     Returns (o, lse, skip_counts): o bf16 [B, H, S, 128], lse float32
     [B, H, S] (or None), skip_counts int32 [B, H, ceil(S/64)] (or None).
-    ``seqlen`` (the length lambda is normalised by) defaults to S.
+    ``seqlen`` (the length lambda is normalised by) defaults to S.  ``out``, if
+    given, receives o and must be a contiguous bf16 tensor shaped like q on
+    q's device.
     """
     _check_qkv(q, k, v, 4)
+    if out is not None:
+        _check_out(out, q)
     B, H, S, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     mode, p0, p1, p2 = _control(factor, threshold, calib)
@@ -171,7 +213,11 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
     length.  Returns (o [T, H, 128], lse [H, T], skip_counts [H, sum ceil(S_b/64)]).
     The skip counts' size comes from the sequence lengths: pass them on the
     host as ``seqlens`` to avoid reading cu_seqlens back from the device
-    (a synchronisation that HIP graph capture does not allow)."""
+    (a synchronisation that HIP graph capture does not allow).  ``seqlens``
+    must equal the lengths cu_seqlens holds on the device; lengths known on
+    the host are checked against q (they must sum to T, and none may exceed
+    max_seqlen).  A sequence longer than max_seqlen would be left unwritten
+    by the kernel."""
     _check_qkv(q, k, v, 3)
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be an int32 1-D tensor on the same device as q")
@@ -179,14 +225,9 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     mode, p0, p1, p2 = _control(factor, threshold, calib)
     nseq = cu_seqlens.numel() - 1
-    if not with_counts:
-        lens = []
-    elif seqlens is not None:
-        lens = [int(n) for n in seqlens]
-        if len(lens) != nseq:
-            raise ValueError(f"seqlens has {len(lens)} entries for {nseq} sequences")
-    else:
-        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).tolist()
+    if nseq < 0:
+        raise ValueError("cu_seqlens must hold at least one entry")
+    lens = _varlen_lengths(cu_seqlens, T, int(max_seqlen), seqlens, read_back=with_counts)
     o = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if with_lse else None
     cnt = None
@@ -334,3 +375,16 @@ def resolve_threshold(mode: int, p0: float, p1: float = 0.0, p2: float = 0.0, se
 def device_check() -> None:
     """Raise SsaError unless the current HIP device is gfx950."""
     _check(load_library().ssa_device_check())
+
+
+def set_vote_poll_limit(polls: int) -> None:
+    """Bound of the wait for the partner wave's half of the vote (polls of
+    one LDS word) for later calls in this process; 16384 by default.  A wave
+    that gives up keeps the tile and its query block's count comes out as
+    -1 - count.  0 forces that path from the host (tests)."""
+    _check(load_library().ssa_set_vote_poll_limit(int(polls)))
+
+
+def vote_poll_limit() -> int:
+    """The current bound of the vote's wait (see set_vote_poll_limit)."""
+    return int(load_library().ssa_vote_poll_limit())

@@ -79,7 +79,8 @@ constexpr int kTileBytes = kBK * kRowBytes;        // 32 KB
 constexpr int kCopyPerWave = kTileBytes / (kWaves * 1024);   // 1 KB DMA instructions per wave per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 16.f;               // P <= 2^16 before a rescale is forced
-constexpr int kSpinLimit = 1 << 14;                 // polls of the partner's vote before giving up
+constexpr int kSpinLimit = 1 << 14;                 // default polls of the partner's vote before giving up
+constexpr int kMaxSpinLimit = 1 << 24;
 constexpr unsigned kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
 constexpr int kXcds = 8;                            // XCDs of an MI355X, each with its own L2
 constexpr int kCompWords = 64;                      // virtual tiles: 32 skip bits per word, up to 2048 tiles
@@ -125,6 +126,7 @@ struct Params {
   float ln_lambda;             // used when lambda_per_seq == 0
   int vote;                    // 0: lambda == 0, nothing is skipped
   int lambda_per_seq;          // 1: ln(lambda_b) = ln(factor / S_b)
+  int spin_limit;              // polls of the partner's half of the vote before the tile is kept
   double factor;
 };
 
@@ -220,6 +222,7 @@ void ssa_fwd_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[2][kFp8 ? kTile8Bytes : kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v[2][kTileBytes];
   __shared__ int vote_lds[kWaves];      // (tile << 1) | pass of the wave's half of the vote
+  __shared__ int vote_timeout[kWaves / 2];   // 1: a wave of the vote group gave up waiting for its partner
   __shared__ float margin_lds[kWaves];  // debug: the wave's margin for the tile
   __shared__ uint32_t comp_bits[kComp ? kWaves / 2 * kCompWords : 1];   // skip bits per vote group
   __shared__ float kscale_lds[kFp8 ? kMaxTilesFp8 : 1];                 // FP8 scores: scale of each K tile
@@ -620,13 +623,20 @@ void ssa_fwd_kernel(const Params p) {
         __hip_atomic_store(&vote_lds[wave], (kt << 1) | (own_pass ? 1 : 0), kPub, __HIP_MEMORY_SCOPE_WORKGROUP);
       // The partner publishes in this same slot; the bound only guards
       // against a wave that never arrives.  Each poll is one LDS round trip;
-      // sleeping between polls measured slightly slower.
+      // sleeping between polls measured slightly slower.  A wave that gives
+      // up keeps the tile (always exact) and flags its vote group, whose
+      // skip count is then stored as -1 - count.
       int pv = 0;
-      for (int spin = 0; spin < kSpinLimit; ++spin) {
+      bool got = false;
+      for (int spin = 0; spin < p.spin_limit; ++spin) {
         pv = __hip_atomic_load(&vote_lds[wave ^ 1], kSub, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if ((pv >> 1) == kt) break;
+        if ((pv >> 1) == kt) {
+          got = true;
+          break;
+        }
       }
-      skip = vote && own_pass && (pv & 1) != 0;
+      if (!got && lane == 0) vote_timeout[wave >> 1] = 1;
+      skip = vote && own_pass && got && (pv & 1) != 0;
       if constexpr (kDebug) {
         if (lane == 0 && (wave & 1) == 0) {
           const long long nqb = (S_b + kBQ - 1) / kBQ;
@@ -691,6 +701,7 @@ void ssa_fwd_kernel(const Params p) {
   // copy into group A's QK^T steps of slot 2j, so it overlaps MFMA work
   // instead of stretching group B's softmax phase.
   if (tid < kWaves) vote_lds[tid] = -2;
+  if (tid < kWaves / 2) vote_timeout[tid] = 0;
   copy_k(0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
@@ -891,11 +902,13 @@ void ssa_fwd_kernel(const Params p) {
   }
   const long long nqb_seq = (S_b + kBQ - 1) / kBQ;
   if (p.counts != nullptr && lane == 0 && (wave & 1) == 0 && qb < nqb_seq) {
+    // the last slot's barrier orders the partner's timeout flag before this read
+    const int cval = vote_timeout[wave >> 1] != 0 ? -1 - nskip : nskip;
     if (p.cu_seqlens != nullptr) {
-      p.counts[(long long)h * qb_total + qb_off + qb] = nskip;
+      p.counts[(long long)h * qb_total + qb_off + qb] = cval;
     } else {
       const long long nqb = (p.S + kBQ - 1) / kBQ;
-      p.counts[((long long)b * p.H + h) * nqb + qb] = nskip;
+      p.counts[((long long)b * p.H + h) * nqb + qb] = cval;
     }
   }
 }
@@ -1053,6 +1066,7 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+std::atomic<int> g_spin_limit{kSpinLimit};   // polls of the vote exchange (a test hook sets it)
 
 int check_device() {
   int dev = -1;
@@ -1195,6 +1209,7 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.scale = scale;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
   p.lambda_per_seq = 0;
+  p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   const dim3 grid(p.qgroups, H, B);
   if (comp) {
     const int nkt = (S + kBK - 1) / kBK;
@@ -1332,6 +1347,7 @@ int ssa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const float* q_scale, cons
   p.scale = scale;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
   p.lambda_per_seq = 0;
+  p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   const dim3 grid(p.qgroups, H, B);
   return tile_mask != nullptr ? launch<true, false, true>(p, grid, static_cast<hipStream_t>(stream))
                               : launch<false, false, true>(p, grid, static_cast<hipStream_t>(stream));
@@ -1374,6 +1390,7 @@ int ssa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* 
   p.seq_stride = 0;
   p.scale = scale;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   if (mode == SSA_MODE_THRESHOLD) {
     p.lambda_per_seq = 0;
   } else {
@@ -1396,6 +1413,15 @@ int ssa_resolve_threshold(int mode, double p0, double p1, double p2, int seqlen,
 }
 
 int ssa_device_check(void) { return check_device(); }
+
+int ssa_set_vote_poll_limit(int polls) {
+  if (polls < 0 || polls > kMaxSpinLimit)
+    return fail(SSA_ERR_INVALID_ARG, "vote poll limit %d outside [0, %d]", polls, kMaxSpinLimit);
+  g_spin_limit.store(polls, std::memory_order_relaxed);
+  return SSA_OK;
+}
+
+int ssa_vote_poll_limit(void) { return g_spin_limit.load(std::memory_order_relaxed); }
 
 const char* ssa_strerror(int status) {
   switch (status) {

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert lib.ssa_version() >= 1
-    for code in (OK, INVALID, UNSUPPORTED, BAD_THRESHOLD, NO_CALIB, DEVICE, -6):
+    for code in (OK, INVALID, UNSUPPORTED, BAD_THRESHOLD, NO_CALIB, DEVICE, -6, -7):
         assert lib.ssa_strerror(code).decode().startswith(ssa.STATUS_NAMES[code])
 
 
@@ -51,13 +51,14 @@ def test_argument_errors_before_any_hip_call(lib):
     assert _fwd(lib, q=None) == INVALID
     assert _fwd(lib, o=FAKE + 8) == INVALID                   # misaligned
     assert _fwd(lib, D=64) == UNSUPPORTED
+    assert "128" in lib.ssa_last_error().decode()
     assert _fwd(lib, B=-1) == INVALID
     assert _fwd(lib, scale=float("nan")) == INVALID
     assert _fwd(lib, scale=-1.0) == INVALID
     assert _fwd(lib, factor=-1.0) == BAD_THRESHOLD
     assert _fwd(lib, factor=float("inf")) == BAD_THRESHOLD
     assert _fwd(lib, seqlen=0) == BAD_THRESHOLD
-    assert "128" in lib.ssa_last_error().decode() or True
+    assert "seqlen" in lib.ssa_last_error().decode()
     assert lib.ssa_fwd_threshold(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, -0.5, None, None) == BAD_THRESHOLD
     # calibrated control without a usable calibration points at the threshold entry
     rc = lib.ssa_fwd_calibrated(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 128, 0.1, 0.0, 4.0, 0.7, 64, None, None)
@@ -160,3 +161,55 @@ def test_fp8_argument_errors(lib):
     assert fwd(margin=FAKE) == INVALID                      # margin without mask
     assert fwd(p0=float("nan")) == BAD_THRESHOLD
     assert fwd(S=0) == OK
+
+
+def test_vote_poll_limit_hook(lib):
+    """The bound of the vote's wait is a process-wide setting checked on the
+    host: 0 .. 2^24 polls, default 16384."""
+    assert ssa.vote_poll_limit() == 16384
+    try:
+        ssa.set_vote_poll_limit(0)
+        assert ssa.vote_poll_limit() == 0
+        for bad in (-1, (1 << 24) + 1):
+            with pytest.raises(ssa.SsaError) as e:
+                ssa.set_vote_poll_limit(bad)
+            assert e.value.code == INVALID
+        assert ssa.vote_poll_limit() == 0
+    finally:
+        ssa.set_vote_poll_limit(16384)
+    assert ssa.vote_poll_limit() == 16384
+
+
+def test_binding_refuses_a_wrong_out():
+    """fwd(out=...) takes only a contiguous bf16 tensor of q's shape on q's
+    device (the kernel writes B*H*S*128 bf16 values in that layout)."""
+    import torch
+    q = torch.empty((1, 2, 64, 128), dtype=torch.bfloat16)
+    ssa._check_out(torch.empty_like(q), q)
+    for bad in (torch.empty((1, 2, 63, 128), dtype=torch.bfloat16),
+                torch.empty((1, 2, 64, 128), dtype=torch.float32),
+                torch.empty((1, 2, 128, 64), dtype=torch.bfloat16).transpose(-1, -2),
+                torch.empty((1, 2, 64, 128), dtype=torch.bfloat16, device="meta"),
+                "not a tensor"):
+        with pytest.raises(ValueError):
+            ssa._check_out(bad, q)
+
+
+def test_binding_checks_varlen_lengths():
+    """Packed-batch lengths known on the host must match the packed tensors:
+    one per sequence, none negative or above max_seqlen, summing to T (the
+    kernel sizes nothing from them, but the skip-count buffer is sized from
+    them and a longer sequence would be left unwritten)."""
+    import torch
+    cu = torch.tensor([0, 100, 100, 350], dtype=torch.int32)
+    assert ssa._varlen_lengths(cu, 350, 250, None, read_back=True) == [100, 0, 250]
+    assert ssa._varlen_lengths(cu, 350, 250, [100, 0, 250], read_back=False) == [100, 0, 250]
+    assert ssa._varlen_lengths(cu, 350, 250, None, read_back=False) is None
+    for T, smax, lens in ((350, 250, [100, 250]),          # too few lengths
+                          (351, 250, [100, 0, 250]),       # lengths do not sum to T
+                          (350, 249, [100, 0, 250]),       # a sequence above max_seqlen
+                          (350, 250, [150, -50, 250])):    # a negative length
+        with pytest.raises(ValueError):
+            ssa._varlen_lengths(cu, T, smax, lens, read_back=False)
+    with pytest.raises(ValueError):
+        ssa._varlen_lengths(cu, 349, 250, None, read_back=True)

@@ -352,3 +352,34 @@ def test_max_prob(ssa, case):
             assert (got <= 1.0).all() and (got >= 1.0 / n_kept * (1 - 1e-3)).all()
     print(f"[case] max_prob {case}: max relative error {worst:.2e}", flush=True)
     assert worst <= 3e-3
+
+
+def test_vote_give_up_keeps_every_tile(ssa):
+    """The bounded wait for the partner wave's half of the vote, driven from
+    the host: with the poll limit at 0 every wave gives up at once, so every
+    tile is kept (the exact path), every query block's count comes out
+    flagged as -1 - 0, the debug mask shows no skipped tile, and O and LSE
+    equal the dense call's bit for bit (the arithmetic of a kept tile does not
+    depend on the vote).  Restoring the limit restores the normal result."""
+    w = inputs.grid_small(41, (4, 12, 20), heads=2)
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    od, lsed, cd = ssa.fwd(q, k, v, scale=w.scale, factor=0.0)
+    o1, l1, c1 = ssa.fwd(q, k, v, scale=w.scale, threshold=0.05)
+    torch.cuda.synchronize()
+    assert int(c1.sum()) > 0 and int(cd.sum()) == 0
+    print(f"[case] vote give-up: normal call skips {int(c1.sum())} tiles", flush=True)
+    try:
+        ssa.set_vote_poll_limit(0)
+        o0, l0, c0 = ssa.fwd(q, k, v, scale=w.scale, threshold=0.05)
+        om, lm, cm, mask, _ = ssa.fwd_debug(q, k, v, scale=w.scale, threshold=0.05)
+        torch.cuda.synchronize()
+    finally:
+        ssa.set_vote_poll_limit(16384)
+    print(f"[case] vote give-up: counts {sorted(set(c0.flatten().tolist()))}, mask skipped {int(mask.sum())}",
+          flush=True)
+    assert (c0 == -1).all() and (cm == -1).all() and int(mask.sum()) == 0
+    assert torch.equal(o0, od) and torch.equal(l0, lsed)
+    assert torch.equal(om, od) and torch.equal(lm, lsed)
+    o2, l2, c2 = ssa.fwd(q, k, v, scale=w.scale, threshold=0.05)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1) and torch.equal(l2, l1) and torch.equal(c2, c1)
