@@ -14,6 +14,15 @@ the same shape as the measured one (3 sequences of 4096, 16384 and 32760
 tokens, H = 16, grid-local generator) but a different seed (5 instead of 4).
 Points with 0.02 < s < 0.98 from all three sequences are pooled.
 
+A single exponential pooled over three lengths lands the longer sequences
+well off the target (ln(factor) is convex in s, and the curves differ by
+length), so the checkpoint layout's per-component curves suggest the second
+fit written here: one (a_S, b_S) per sequence length, an OLS of
+ln(factor) = ln(a_S) + b_S * s through that length's calibration curve read
+at the targets (ln(factor) interpolated linearly between sweep points).  For
+both fits the skip fraction each target reaches on the calibration data is
+recomputed exactly (closed form or recurrence, as for the sweep).
+
 The skip fraction at one factor comes from the oracle only:
   * lambda_b <= 1: the closed-form prefix-maximum margins
     (oracle.prefix_max_margins_head) of 16 seeded query blocks per head;
@@ -61,6 +70,7 @@ def main():
     rng = np.random.default_rng(4321)
     points = []
     detail = {}
+    skip_at = {}
     for S, q, k, v in seqs:
         nqb = -(-S // oracle.BLOCK_Q)
         margins = np.concatenate([
@@ -70,7 +80,7 @@ def main():
         heads = np.sort(rng.choice(HEADS, 8, replace=False))
         units = [(h, np.sort(rng.choice(nqb, 4, replace=False))) for h in heads]
 
-        def frac_recurrence(ln_lam):
+        def frac_recurrence(ln_lam, q=q, k=k, v=v, units=units):
             tot = sk = 0
             for h, qbs in units:
                 r = oracle.skip_head(q[h], k[h], v[h], w.scale, ln_lam, qblocks=qbs)
@@ -78,17 +88,18 @@ def main():
                 sk += int(r.skipped.sum())
             return sk / tot
 
-        rows = []
-        for e in LOG2_FACTORS:
-            factor = 2.0 ** e
+        def frac_at(factor, S=S, margins=margins, frac_recurrence=frac_recurrence):
             lam = oracle.resolve_lambda(factor=factor, seqlen=S)
             ln = oracle.ln_lambda_f32(lam)
             if lam <= 1.0:
-                s = float((margins < ln).mean())
-                how = "closed form"
-            else:
-                s = frac_recurrence(ln)
-                how = "recurrence"
+                return lam, float((margins < ln).mean()), "closed form"
+            return lam, frac_recurrence(ln), "recurrence"
+
+        skip_at[S] = frac_at
+        rows = []
+        for e in LOG2_FACTORS:
+            factor = 2.0 ** e
+            lam, s, how = frac_at(factor)
             rows.append({"factor": factor, "lambda": lam, "skip": s, "method": how})
             if S_LO < s < S_HI:
                 points.append((s, math.log(factor)))
@@ -102,12 +113,28 @@ def main():
     ln_a = float(y.mean() - b * x.mean())
     a = math.exp(ln_a)
     resid = y - (ln_a + b * x)
+    pooled_reached = {str(S): {str(t): skip_at[S](a * math.exp(b * t))[1] for t in TARGETS} for S, *_ in seqs}
+    per_length = {}
+    for S, *_ in seqs:
+        rows = detail[str(S)]
+        lf = np.log([r["factor"] for r in rows])
+        sk = np.maximum.accumulate(np.array([r["skip"] for r in rows]))   # a monotone reading of the curve
+        yt = np.array([float(np.interp(t, sk, lf)) for t in TARGETS])
+        xt = np.array(TARGETS)
+        bS = float(((xt - xt.mean()) * (yt - yt.mean())).sum() / ((xt - xt.mean()) ** 2).sum())
+        aS = math.exp(float(yt.mean() - bS * xt.mean()))
+        reached = {str(t): skip_at[S](aS * math.exp(bS * t))[1] for t in TARGETS}
+        per_length[str(S)] = {"a": aS, "b": bS, "reached_on_calibration": reached}
+        print(f"S={S}: per-length a = {aS:.6g}, b = {bS:.6g}; reached {reached}", flush=True)
     out = {
         "workload": "calibration batch: varlen S = 4096, 16384, 32760 (grids 4x32x32, 16x32x32, 21x30x52), "
                     f"H = {HEADS}, D = 128, seed {FIT_SEED}",
         "fit": "OLS of ln(factor) on skipped-tile fraction, points with 0.02 < s < 0.98 pooled over sequences",
         "a": a, "b": b, "n_points": len(points), "rms_residual_ln_factor": float(np.sqrt((resid ** 2).mean())),
         "factor_at_target": {str(t): a * math.exp(b * t) for t in TARGETS},
+        "reached_on_calibration": pooled_reached,
+        "per_length_fit": "OLS of ln(factor) on s through each length's calibration curve read at the targets",
+        "per_length": per_length,
         "sweep": detail,
         "seconds": round(time.time() - t0, 1),
     }

@@ -69,6 +69,42 @@ def compare_head_blocks(qd, kd, vd, scale, ln_lambda, qblocks, gpu_mask, gpu_o, 
                   o_max=float(err.max()), o_mean=float(err.mean()), lse_max=float(lerr.max()))
 
 
+def whole_head_mask_closed_form(gpu_mask, margins, ln_lambda):
+    """Every tile of a head, lambda <= 1: the GPU's decisions [nQB, nKT]
+    against the closed form margin < ln(lambda) with the dense prefix-maximum
+    margins (oracle.prefix_max_margins_head).  Tiles within MASK_BAND of
+    ln(lambda) may differ; everything else must be identical.  Returns
+    (tiles compared exactly, tiles exempt and different)."""
+    want = margins < np.float32(ln_lambda)
+    band = np.abs(margins.astype(np.float64) - float(ln_lambda)) <= MASK_BAND
+    diff = gpu_mask != want
+    bad = diff & ~band
+    assert not bad.any(), (f"{int(bad.sum())} tile decisions differ outside the band "
+                           f"(first at {np.argwhere(bad)[:3].tolist()})")
+    return int((~band).sum()), int((diff & band).sum())
+
+
+def whole_head_mask_recurrence(gpu_mask, skipped, margins, ln_lambda):
+    """Every tile of a head, any lambda: the GPU's decisions [nQB, nKT]
+    against the recurrence's own (the single-precision C oracle's decisions
+    and margins).  Above lambda = 1 a kept tile can raise the running
+    maximum, so after a decision that differs inside the band the two sides
+    run on different maxima: the rest of that query block is exempt (and
+    counted).  Returns (tiles compared exactly, tiles exempt)."""
+    band = np.abs(margins.astype(np.float64) - float(ln_lambda)) <= MASK_BAND
+    exact = exempt = 0
+    for qb in range(gpu_mask.shape[0]):
+        diff = np.nonzero(gpu_mask[qb] != skipped[qb])[0]
+        stop = gpu_mask.shape[1]
+        if diff.size:
+            first = int(diff[0])
+            assert band[qb, first], f"query block {qb}: tile {first} differs outside the band"
+            stop = first
+        exact += stop
+        exempt += gpu_mask.shape[1] - stop
+    return exact, exempt
+
+
 def merge(reports: Sequence[Report]) -> Report:
     n = sum(r.tiles for r in reports)
     return Report(tiles=n, skipped=sum(r.skipped for r in reports), exempt=sum(r.exempt for r in reports),

@@ -3,9 +3,10 @@
 The quantiser is integer work: codes and scales must equal the oracle's
 (oracle/fp8.py) bit for bit.  The attention is compared with the oracle's
 recurrence run on the dequantised operands.  The E4M3 MFMA does not sum its
-products exactly: on the box it was measured to stay within about 2^-12 of
-the sum of the products' magnitudes (random codes over the full range).  The
-bound used here is EPS = 2^-10 of that sum, per score (oracle.fp8.score_error_bound):
+products exactly: it stays within about 2^-12 of the sum of the products'
+magnitudes (random codes over the full range), which
+test_fp8_mfma_dot_error_within_eps measures on every run.  The bound used
+here is EPS = 2^-10 of that sum, per score (oracle.fp8.score_error_bound):
   * mask: identical to the oracle outside a band of 1e-3 plus twice the largest
     bound of the block's rows (the margin is a difference of two scores);
   * O: against the oracle forced to the GPU's mask, the bars of tests/parity.py;
@@ -110,6 +111,49 @@ def _check_attention(ssa, w, name, qblocks=None, heads=None, **kw):
     assert err.max() <= parity.O_MAX and err.mean() <= parity.O_MEAN
     assert lover.max() <= 0.0
     return mask
+
+
+def test_fp8_mfma_dot_error_within_eps(ssa):
+    """The E4M3 MFMA's summation error, measured on every run against the
+    bound the FP8 tests use: |computed - exact| <= EPS * sum |q_d k_d| (times
+    the scales).  Each of 4096 heads holds one query and one key (S = 1), so
+    the kernel's LSE is exactly its one score, up to float rounding of the
+    score factor and the exponent reference (about 1e-6 of the score, which
+    the sum of magnitudes bounds).  Half the heads use E4M3 codes drawn
+    uniformly over every finite code (one element of each row set to 448, so
+    the scale is 1 and the codes pass through the quantiser unchanged), half
+    use normal values times 2^U(-8, 0) (a wide spread of exponents in every
+    dot product).  The exact dot product of decoded codes is exact in
+    float64."""
+    rng = np.random.default_rng(90)
+    H, D = 4096, 128
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = np.empty((2, H, D))
+    for i in range(2):
+        codes = rng.choice(finite, size=(H // 2, D))
+        x = ofp8.e4m3_decode(codes)
+        x[:, 0] = 448.0
+        vals[i, : H // 2] = x
+        vals[i, H // 2:] = rng.standard_normal((H // 2, D)) * np.exp2(rng.uniform(-8, 0, (H // 2, D)))
+    t = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).reshape(1, H, 1, D).cuda()
+    q, k = t(vals[0]), t(vals[1])
+    v = torch.ones_like(q)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    q8, k8, qs, ks = ssa.quantize_qk_fp8(q, k)
+    _, lse, _ = ssa.fwd_fp8(q8, k8, qs, ks, v, scale=scale, factor=0.0)
+    torch.cuda.synchronize()
+    dq = ofp8.e4m3_decode(q8.cpu().numpy().reshape(H, D))
+    dk = ofp8.e4m3_decode(k8.cpu().numpy().reshape(H, D))
+    fac = scale * qs.cpu().numpy().reshape(H).astype(np.float64) * ks.cpu().numpy().reshape(H).astype(np.float64)
+    exact = fac * (dq * dk).sum(axis=1)
+    unit = fac * np.abs(dq * dk).sum(axis=1)
+    assert (q8.cpu().numpy().reshape(H, D)[: H // 2] == ofp8.e4m3_encode(vals[0, : H // 2].astype(np.float32))).all()
+    ratio = np.abs(lse.cpu().numpy().reshape(H).astype(np.float64) - exact) / unit
+    print(f"[case] fp8 MFMA dot error: max {ratio.max():.3e} = 2^{np.log2(ratio.max()):.2f} of sum|ab| "
+          f"(uniform codes {ratio[: H // 2].max():.3e}, spread normals {ratio[H // 2:].max():.3e}); bound EPS = 2^-10",
+          flush=True)
+    assert np.isfinite(ratio).all()
+    assert ratio.max() <= EPS
 
 
 def test_quantize_tiny(ssa):

@@ -4,6 +4,10 @@ The oracle cannot do the whole 22 TFLOP problem on the CPU, so each case
 checks every output that is cheap to check and samples the rest:
   * determinism and product/debug agreement over the whole problem;
   * skip_counts equal to the debug mask's row sums everywhere;
+  * the tile mask of whole heads (every query block and tile) against the
+    oracle: for lambda <= 1 the closed form with the dense prefix maximum
+    (oracle.prefix_max_margins_head), above 1 the single-precision C
+    recurrence's own decisions (its decisions-only mode);
   * tile mask, O and LSE against the oracle on seeded samples of query blocks
     (rows are independent given K and V, so a sampled block is exact),
     against both oracles (float64 numpy and the single-precision C
@@ -72,6 +76,30 @@ def _sampled(w, ln, o, lse, cnt, mask, heads, per_head, seed, ref=None):
     return parity.merge(reports)
 
 
+_MARGINS = {}   # (workload, head) -> prefix-maximum margins of that head (they do not depend on lambda)
+
+
+def _whole_heads(name, w, mask, ln, lam, heads, b=0):
+    """Compare the GPU mask of every query block of the listed heads with the
+    oracle; returns (heads, tiles compared exactly, exempt tiles)."""
+    exact = exempt = 0
+    for h in heads:
+        qd, kd = oracle.from_bf16(w.q[b, h]), oracle.from_bf16(w.k[b, h])
+        if lam <= 1.0:
+            key = (name, b, h)
+            if key not in _MARGINS:
+                _MARGINS[key] = oracle.prefix_max_margins_head(qd, kd, w.scale)
+            e, x = parity.whole_head_mask_closed_form(mask[b, h], _MARGINS[key], ln)
+        else:
+            sk, mg = c_oracle.oracle().skip_mask(qd, kd, w.scale, ln)
+            e, x = parity.whole_head_mask_recurrence(mask[b, h], sk, mg, ln)
+        exact += e
+        exempt += x
+        print(f"[whole head] {name} head {h}: {mask[b, h].shape[0]} query blocks, skip fraction "
+              f"{mask[b, h].mean():.4f}, {e} tiles exact, {x} exempt", flush=True)
+    return len(heads), exact, exempt
+
+
 def _lam(frac):
     with open(os.path.join(GOLDEN, "wan_lambdas.json")) as f:
         return json.load(f)["lambda"][frac]
@@ -85,6 +113,10 @@ def test_wan_like(ssa, wan, frac):
     q, k, v = (t.cuda() for t in (wan.q, wan.k, wan.v))
     o, lse, cnt, mask = _whole_problem_checks(ssa, q, k, v, wan.scale, factor=lam * S)
     ln = oracle.ln_lambda_f32(oracle.resolve_lambda(factor=lam * S, seqlen=S))
+    if lam > 0:
+        heads = (0, 13, 26, 39) if lam <= 1.0 else (0, 39)
+        nh, exact, exempt = _whole_heads("wan", wan, mask, ln, lam, heads)
+        print(f"[case] wan-like {frac}: {nh} whole heads, {exact} tiles exact, {exempt} exempt", flush=True)
     rep = _sampled(wan, ln, o, lse, cnt, mask, heads=(0, 17, 39), per_head=6, seed=int(float(frac) * 100))
     print(f"[case] wan-like {frac}: whole-problem skip fraction {mask.mean():.4f}; sampled {rep}", flush=True)
     parity.assert_bar(rep)
@@ -106,6 +138,11 @@ def test_long_sequence(ssa):
         print(f"[case] long S={S} H=24 threshold {lam}", flush=True)
         o, lse, cnt, mask = _whole_problem_checks(ssa, q, k, v, w.scale, threshold=lam)
         ln = oracle.ln_lambda_f32(lam)
+        if lam > 0:
+            nh, exact, exempt = _whole_heads("long", w, mask, ln, lam, (0, 8, 16, 23))
+            print(f"[case] long {lam}: {nh} whole heads, {exact} tiles exact, {exempt} exempt", flush=True)
+        else:
+            assert not mask.any()
         rep = _sampled(w, ln, o, lse, cnt, mask, heads=(0, 23), per_head=6, seed=3)
         print(f"[case] long {lam}: whole-problem skip fraction {mask.mean():.4f}; sampled {rep}", flush=True)
         parity.assert_bar(rep)
@@ -156,8 +193,10 @@ def test_calibrated_varlen(ssa, varlen_batch, target):
         assert torch.equal(cnt[:, off:off + nqb], cd[0]), f"sequence {bi}: packed counts differ"
         mask_np = mask.cpu().numpy().astype(bool)
         achieved.append(float(mask_np.mean()))
-        ln = oracle.ln_lambda_f32(oracle.resolve_lambda(a=a, b=b, target_sparsity=target, seqlen=n))
+        lam_b = oracle.resolve_lambda(a=a, b=b, target_sparsity=target, seqlen=n)
+        ln = oracle.ln_lambda_f32(lam_b)
         seq_w = inputs.Workload("seq", qs, ks, vs, scale=w.scale)
+        _whole_heads(f"varlen{n}", seq_w, mask_np, ln, lam_b, (bi * 7 % 16,))
         reports.append(_sampled(seq_w, ln, od, ld, cd, mask_np, heads=(0, 15), per_head=4, seed=100 + bi))
         reports.append(_sampled(seq_w, ln, od, ld, cd, mask_np, heads=(0, 15), per_head=4, seed=100 + bi,
                                 ref=c_oracle.oracle().skip_head))
@@ -166,5 +205,24 @@ def test_calibrated_varlen(ssa, varlen_batch, target):
     print(f"[case] calibrated varlen target {target}: achieved skip fraction per sequence "
           + ", ".join(f"S={n}: {f:.4f}" for n, f in zip(w.seqlens, achieved)) + f"; sampled {rep}", flush=True)
     parity.assert_bar(rep)
-    # the fit pools all three lengths, so each sequence lands near, not on, the target
-    assert all(abs(f - target) < 0.2 for f in achieved)
+    # The pooled fit lands each sequence near, not on, the target: as near as
+    # it lands on its own calibration data, with 0.04 for the other seed.
+    tol_pooled = max(abs(x - t) for per in cal["reached_on_calibration"].values()
+                     for t, x in ((float(t), x) for t, x in per.items())) + 0.04
+    assert all(abs(f - target) <= tol_pooled for f in achieved), (achieved, tol_pooled)
+    # The per-length fit (one curve per sequence length) on the same sequences,
+    # each run alone with the fixed-length calibrated entry.
+    per_len, tol_len = [], 0.0
+    seqs = zip(*(inputs.unpack_varlen(t, w.cu_seqlens) for t in (w.q, w.k, w.v)))
+    for bi, (qs, ks, vs) in enumerate(seqs):
+        n = w.seqlens[bi]
+        fit = cal["per_length"][str(n)]
+        tol_len = max(tol_len, max(abs(x - float(t)) for t, x in fit["reached_on_calibration"].items()))
+        _, _, c_b = ssa.fwd(qs.cuda(), ks.cuda(), vs.cuda(), scale=w.scale, calib=(fit["a"], fit["b"], target), seqlen=n)
+        torch.cuda.synchronize()
+        per_len.append(float(c_b.sum()) / (c_b.numel() * -(-n // 128)))
+    tol_len += 0.04
+    print(f"[case] calibrated varlen target {target}: per-length fit reaches "
+          + ", ".join(f"S={n}: {f:.4f}" for n, f in zip(w.seqlens, per_len))
+          + f" (bar {tol_len:.3f}); pooled fit bar {tol_pooled:.3f}", flush=True)
+    assert all(abs(f - target) <= tol_len for f in per_len), (per_len, tol_len)
