@@ -19,17 +19,29 @@ the long sequence with sink keys at lambda = 1e-3, the calibrated varlen batch
 at target sparsity 0.5, 0.7 and 0.9), each paired with its own lambda = 0
 call; and the CPU oracle timed on a bounded sample as a baseline only.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15]
+Kernel durations come from two clocks.  Before the parent process touches
+the GPU it runs itself once under rocprofv3 --kernel-trace --stats
+(``--counters trace``: the same dense and skip calls, interleaved, on the
+same inputs), and the traced mean duration of each kernel instance goes
+into ``rocprof``; ``roofline`` is computed from the traced skip kernel.  The
+timed loop itself is bracketed by HIP events on the launch stream
+(``skip_step``, ``dense_step``, ``ms_per_step``, and ``roofline.achieved_events``).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15] [--no-trace]
     python bench.py --power 200      # socket power and energy per call instead
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import math
 import os
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +50,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak (published)
 METRIC = "effective TFLOP/s + MFMA util at S=32760 H=40 D=128, and speedup vs λ=0 at ~75% skip"
 KERNEL_SRC = os.path.join(ROOT, "skip_softmax_flashattention_amd", "csrc", "ssa_fwd.hip")
+KERNEL_DENSE = "ssa_fwd_kernel<false, false, false, true>"    # the lambda = 0 instance
+KERNEL_SKIP = "ssa_fwd_kernel<false, false, false, false>"    # the instance with the skip test
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wan_like.json")
 
 
@@ -64,6 +78,86 @@ def issued_mfma_flops(mask, D=128, bq=64, bk=128):
     tiles = mask.size
     kept = int((~mask).sum())
     return 2.0 * D * bq * bk * (tiles + kept)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def rocprof_trace(steps, warmup, timeout=600):
+    """Run this script under rocprofv3 --kernel-trace --stats (the dense and
+    skip calls of the headline workload, interleaved) and return the traced
+    mean duration of each ssa_fwd_kernel instance, or None when rocprofv3 is
+    missing or wrote no statistics.  rocprofv3 can end with a segmentation
+    fault after the program and its files are complete; the statistics are
+    used whenever they were written."""
+    exe = shutil.which("rocprofv3") or ("/opt/rocm/bin/rocprofv3" if os.path.exists("/opt/rocm/bin/rocprofv3") else None)
+    if exe is None:
+        return None
+    out_dir = tempfile.mkdtemp(prefix="ssa_trace_")
+    cmd = [exe, "--kernel-trace", "--stats", "--output-format", "csv", "-d", out_dir, "-o", "bench", "--",
+           sys.executable, os.path.abspath(__file__), "--counters", "trace", "--steps", str(steps),
+           "--warmup", str(warmup)]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout, cwd=tempfile.gettempdir(),
+                           env={**os.environ, "TMPDIR": tempfile.gettempdir()})
+        stats = os.path.join(out_dir, "bench_kernel_stats.csv")
+        if not os.path.exists(stats):
+            print(f"bench: rocprofv3 wrote no kernel statistics (exit {r.returncode})", file=sys.stderr)
+            return None
+        kernels = {}
+        with open(stats) as f:
+            for row in csv.DictReader(f):
+                name = row["Name"]
+                if "ssa_fwd_kernel<" in name:
+                    key = "ssa_fwd_kernel<" + name.split("ssa_fwd_kernel<", 1)[1].split(">", 1)[0] + ">"
+                    kernels[key] = {"calls": int(row["Calls"]), "mean_ms": float(row["AverageNs"]) / 1e6,
+                                    "min_ms": float(row["MinNs"]) / 1e6, "max_ms": float(row["MaxNs"]) / 1e6}
+        return {"command": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o bench -- python3 bench.py "
+                           f"--counters trace --steps {steps} --warmup {warmup}",
+                "exit_code": r.returncode, "kernels": kernels}
+    except (subprocess.TimeoutExpired, OSError, KeyError, ValueError) as e:
+        print(f"bench: rocprofv3 trace failed: {e}", file=sys.stderr)
+        return None
+    finally:
+        shutil.rmtree(out_dir, ignore_errors=True)
+
+
+def cpu_full_configs():
+    """The oracle's recurrence (plain C, single precision) on the two small
+    workloads in full: Tiny at each of its factors, Mid at threshold 1e-3."""
+    import numpy as np
+    import oracle
+    from oracle import c_oracle
+    from skip_softmax_flashattention_amd import inputs
+    orc = c_oracle.oracle()
+    out = {}
+    for name, w, controls in (("tiny", inputs.tiny(), [("factor", f) for f in (0.0, 0.5, 4.0)]),
+                              ("mid", inputs.mid(), [("threshold", 1e-3)])):
+        B, H, S, D = w.q.shape
+        heads = [tuple(oracle.from_bf16(t[b, h]) for t in (w.q, w.k, w.v)) for b in range(B) for h in range(H)]
+        nkt = -(-S // 128)
+        c = np.minimum(128, S - 128 * np.arange(nkt)).astype(np.float64)
+        r_ = np.minimum(64, S - 64 * np.arange(-(-S // 64))).astype(np.float64)
+        for kind, x in controls:
+            lam = oracle.resolve_lambda(factor=x, seqlen=S) if kind == "factor" else oracle.resolve_lambda(threshold=x)
+            ln = oracle.ln_lambda_f32(lam)
+            t0 = time.perf_counter()
+            fl = 0.0
+            for qd, kd, vd in heads:
+                res = orc.skip_head(qd, kd, vd, w.scale, ln)
+                fl += 2.0 * D * (r_[:, None] * c[None, :] * (1 + (~res.skipped))).sum()
+            dt = time.perf_counter() - t0
+            out[f"{name}_{kind}_{x:g}"] = {"seconds": round(dt, 3), "tflops": round(float(fl) / dt / 1e12, 6),
+                                           "executed_gflop": round(float(fl) / 1e9, 3)}
+    return out
 
 
 def cpu_baseline(w, ln_lambda, seconds):
@@ -104,8 +198,10 @@ def cpu_baseline(w, ln_lambda, seconds):
         blocks += n
         heads += 1
     return {"value": round(tot_fl / tot_dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{blocks} query blocks (64 rows x all 256 key tiles) over the first {heads} head(s), seeded, "
-                      f"at the same lambda; plain-C float32 recurrence (gcc -O2, OpenMP), {tot_dt:.1f} s"}
+                      f"at the same lambda; plain-C float32 recurrence (gcc -O2, OpenMP), {tot_dt:.1f} s",
+            "full_configs": cpu_full_configs()}
 
 
 def copy_reference(launches):
@@ -181,14 +277,22 @@ def main():
     ap.add_argument("--power", type=int, default=0, metavar="CALLS",
                     help="instead of the benchmark: socket power (hwmon, read-only) over CALLS back-to-back dense "
                          "and then skip calls")
-    ap.add_argument("--counters", choices=("dense", "skip", "copy"), default=None,
-                    help="launch only one configuration (or the plain copy reference), for rocprofv3 --pmc")
+    ap.add_argument("--counters", choices=("dense", "skip", "copy", "trace"), default=None,
+                    help="launch only one configuration (or the plain copy reference), for rocprofv3 --pmc; "
+                         "'trace' launches the dense and skip calls interleaved, for the kernel trace")
+    ap.add_argument("--no-trace", action="store_true", help="skip the rocprofv3 kernel-trace child run")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "multi-GPU sharding of this kernel is not built", file=sys.stderr)
         sys.exit(2)
+
+    # The kernel trace runs first, in a child process, before this process
+    # makes any GPU call.
+    trace = None
+    if args.counters is None and args.power == 0 and not args.no_trace:
+        trace = rocprof_trace(args.steps, args.warmup)
 
     import numpy as np
     import torch
@@ -214,6 +318,16 @@ def main():
     if args.power > 0:
         print(json.dumps({"power_run": power_run(ssa, q, k, v, w.scale, factor, args.power),
                           "workload": "wan-like B=1 H=40 S=32760 D=128", "lambda": lam,
+                          "kernel_sha256_16": kernel_hash()}), flush=True)
+        return
+
+    if args.counters == "trace":
+        # The timed loop's calls, interleaved, with nothing else: warmup + steps pairs.
+        for _ in range(args.warmup + args.steps):
+            ssa.fwd(q, k, v, factor=0.0, scale=w.scale)
+            ssa.fwd(q, k, v, factor=factor, scale=w.scale)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": "trace", "launches": 2 * (args.warmup + args.steps),
                           "kernel_sha256_16": kernel_hash()}), flush=True)
         return
 
@@ -405,6 +519,30 @@ def main():
     others["varlen_workload"] = f"H={qv.shape[1]} S_b={lens}, calibrated a={cal['a']:.5f} b={cal['b']:.4f}, seed 4"
     del qv, kv, vv, wv
 
+    # Roofline of the skip kernel: executed FLOP over its traced mean duration
+    # (rocprofv3), else over the HIP-event mean of the timed loop.
+    t_trace_s = t_trace_d = None
+    if trace is not None:
+        ks = trace["kernels"]
+        if KERNEL_SKIP in ks and KERNEL_DENSE in ks:
+            t_trace_s, t_trace_d = ks[KERNEL_SKIP]["mean_ms"], ks[KERNEL_DENSE]["mean_ms"]
+    t_roof = t_trace_s if t_trace_s is not None else t_s
+    exe_roof = exec_flops / (t_roof * 1e-3) / 1e12
+    rocprof = None
+    if trace is not None:
+        rocprof = dict(trace)
+        if t_trace_s is not None:
+            rocprof.update({
+                "skip_kernel_mean_ms": round(t_trace_s, 4), "dense_kernel_mean_ms": round(t_trace_d, 4),
+                "skip_executed_tflops": round(exec_flops / (t_trace_s * 1e-3) / 1e12, 2),
+                "skip_effective_tflops": round(dense_flops / (t_trace_s * 1e-3) / 1e12, 2),
+                "skip_mfma_util_issued": round(mfma_flops / (t_trace_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "dense_tflops": round(dense_flops / (t_trace_d * 1e-3) / 1e12, 2),
+                "dense_mfma_util": round(dense_flops / (t_trace_d * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "speedup_vs_dense": round(t_trace_d / t_trace_s, 4)})
+        rocprof["kernels"] = {k_: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v_.items()}
+                              for k_, v_ in rocprof["kernels"].items()}
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -432,12 +570,18 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "achieved": round(exe, 2),
+            "achieved": round(exe_roof, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(exe / PEAK_BF16_TFLOPS, 4),
+            "frac": round(exe_roof / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
+            "kernel": KERNEL_SKIP,
+            "timing": "rocprofv3 kernel trace" if t_trace_s is not None else "hip events",
+            "kernel_ms": round(t_roof, 4),
+            "achieved_events": round(exe, 2),
+            "frac_events": round(exe / PEAK_BF16_TFLOPS, 4),
         },
+        "rocprof": rocprof,
         "skip_step": {
             "ms_mean": round(t_s, 4), "ms_min": round(float(ms_skip.min()), 4),
             "ms_median": round(float(np.median(ms_skip)), 4),

@@ -67,6 +67,13 @@ def test_bench_json_line():
     assert len(oc["varlen_calibrated_0.9"]["skip_fraction_per_sequence"]) == 3
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert cpu["cpu_model"] and {"tiny_factor_4", "mid_threshold_0.001"} <= set(cpu["full_configs"])
+    # kernel durations from the rocprofv3 child run: the roofline uses the traced skip kernel,
+    # whose duration cannot exceed the HIP-event time of the same call
+    tr = d["rocprof"]
+    assert tr is not None and roof["timing"] == "rocprofv3 kernel trace"
+    assert tr["kernels"][bench.KERNEL_SKIP]["calls"] == 3 and tr["kernels"][bench.KERNEL_DENSE]["calls"] == 3
+    assert roof["kernel_ms"] == tr["skip_kernel_mean_ms"] <= 1.05 * d["ms_per_step"]
 
 
 @pytest.mark.gpu
