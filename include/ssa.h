@@ -85,6 +85,7 @@ typedef enum {
 #define SSA_HEAD_DIM 128
 #define SSA_BLOCK_Q 64
 #define SSA_BLOCK_K 128
+#define SSA_VIRTUAL_NOALLOC_BYTES (16u << 20)   /* static workspace of ssa_fwd_virtual_noalloc */
 
 /* lambda = factor / seqlen.  factor >= 0 and finite, seqlen > 0 (normally S). */
 int ssa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -156,6 +157,23 @@ int ssa_fwd_virtual(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int S, int D, float scale, int mode, double p0, double p1,
                     double p2, int seqlen, int32_t* skip_counts, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* ssa_fwd_virtual for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call without the workspace argument.  The tile means go to a static device
+ * array of the library, SSA_VIRTUAL_NOALLOC_BYTES = 16 MiB, one per GPU,
+ * held until the process ends; its address is looked up once per
+ * device, on the first call there.  The call must fit it: B * H *
+ * ceil(S/128) * 768 bytes <= 16 MiB, i.e. at most 21845 (batch, head, key
+ * tile) triples, else SSA_ERR_UNSUPPORTED before any HIP call.  Every call
+ * on one GPU uses the same array, and every byte a call reads from it is
+ * written earlier in the same call, so nothing needs clearing between calls;
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it and must not be issued.  Allocates nothing and calls no allocating
+ * routine; the caller passes inputs and outputs as for ssa_fwd_virtual. */
+int ssa_fwd_virtual_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int S, int D, float scale, int mode, double p0, double p1,
+                            double p2, int seqlen, int32_t* skip_counts, void* stream);
 
 /* FP8 scores.  The score matmul Q K^T runs on 8-bit floating point at the
  * doubled matrix rate while P.V keeps bf16 inputs (video-attention blog post

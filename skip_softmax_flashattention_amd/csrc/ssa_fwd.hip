@@ -57,6 +57,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -64,6 +65,14 @@
 #include <type_traits>
 
 #include "ssa.h"
+
+// Workspace of ssa_fwd_virtual_noalloc (the per-tile mean keys and values),
+// for callers that cannot allocate: one array per GPU, held until the
+// process ends.  Host code never passes this name to a kernel or a copy (on
+// the host it is only a stand-in for the symbol): it uses the device address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = SSA_VIRTUAL_NOALLOC_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -1067,6 +1076,32 @@ int fail(int code, const char* fmt, ...) {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
 std::atomic<int> g_spin_limit{kSpinLimit};   // polls of the vote exchange (a test hook sets it)
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];                 // device address of `scratch` on each device, once looked up
+
+// The device address of the static workspace on the current device, looked
+// up once per device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(SSA_ERR_DEVICE, "no HIP device is available");
+  }
+  if (dev >= kMaxDevices) return fail(SSA_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return fail(SSA_ERR_LAUNCH, "hipGetSymbolAddress of the static workspace failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SSA_OK;
+}
 
 int check_device() {
   int dev = -1;
@@ -1159,7 +1194,8 @@ int launch(const Params& p, dim3 grid, hipStream_t stream) {
 int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, float* maxp, int B, int H, int S,
               int D,
               float scale, int mode, double p0, double p1, double p2, int seqlen, int32_t* counts, uint8_t* mask,
-              float* margin, void* stream, bool debug, void* comp_ws = nullptr, size_t comp_ws_bytes = 0) {
+              float* margin, void* stream, bool debug, void* comp_ws = nullptr, size_t comp_ws_bytes = 0,
+              bool static_ws = false) {
   int st = check_tensors(q, k, v, o, lse, H, D, scale);
   if (st != SSA_OK) return st;
   if (B < 0 || S < 0) return fail(SSA_ERR_INVALID_ARG, "negative batch or sequence length");
@@ -1171,12 +1207,20 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (margin != nullptr && !aligned(margin, 4)) return fail(SSA_ERR_INVALID_ARG, "tile_margin must be 4-byte aligned");
   if (maxp != nullptr && !aligned(maxp, 4)) return fail(SSA_ERR_INVALID_ARG, "max_prob must be 4-byte aligned");
   if (debug && mask == nullptr) return fail(SSA_ERR_INVALID_ARG, "tile_mask must not be NULL");
-  const bool comp = comp_ws != nullptr;
+  const bool comp = comp_ws != nullptr || static_ws;
   if (comp) {
-    if (!aligned(comp_ws, 16)) return fail(SSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    if (comp_ws_bytes < comp_workspace_bytes(B, H, S))
-      return fail(SSA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed", comp_ws_bytes,
-                  comp_workspace_bytes(B, H, S));
+    if (static_ws) {
+      if (comp_workspace_bytes(B, H, S) > kScratchBytes)
+        return fail(SSA_ERR_UNSUPPORTED,
+                    "the tile means of this call need %zu bytes, above the %zu-byte static workspace "
+                    "(B x H x ceil(S / 128) <= %zu); use ssa_fwd_virtual with a workspace",
+                    comp_workspace_bytes(B, H, S), kScratchBytes, kScratchBytes / (3 * kD * sizeof(uint16_t)));
+    } else {
+      if (!aligned(comp_ws, 16)) return fail(SSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+      if (comp_ws_bytes < comp_workspace_bytes(B, H, S))
+        return fail(SSA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed", comp_ws_bytes,
+                    comp_workspace_bytes(B, H, S));
+    }
     if ((S + kBK - 1) / kBK > 32 * kCompWords)
       return fail(SSA_ERR_UNSUPPORTED, "virtual tiles support at most %d key tiles (S <= %d)", 32 * kCompWords,
                   32 * kCompWords * kBK);
@@ -1187,6 +1231,10 @@ int fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (B == 0 || H == 0 || S == 0) return SSA_OK;
   st = check_device();
   if (st != SSA_OK) return st;
+  if (static_ws) {
+    st = scratch_address(&comp_ws);
+    if (st != SSA_OK) return st;
+  }
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -1272,6 +1320,13 @@ int ssa_fwd_virtual(const void* q, const void* k, const void* v, void* o, float*
   if (workspace == nullptr) return fail(SSA_ERR_INVALID_ARG, "workspace must not be NULL");
   return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, nullptr,
                    nullptr, stream, false, workspace, workspace_bytes);
+}
+
+int ssa_fwd_virtual_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
+                            int D, float scale, int mode, double p0, double p1, double p2, int seqlen,
+                            int32_t* skip_counts, void* stream) {
+  return fwd_fixed(q, k, v, o, lse, nullptr, B, H, S, D, scale, mode, p0, p1, p2, seqlen, skip_counts, nullptr,
+                   nullptr, stream, false, nullptr, 0, true);
 }
 
 int ssa_quantize_qk_fp8(const void* q, const void* k, uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale,
