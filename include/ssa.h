@@ -40,8 +40,9 @@
  *   skip_counts   int32 [B, H, ceil(S/64)]: number of skipped key tiles of
  *                 each 64-row query block. May be NULL.  The two waves of a
  *                 block exchange their halves of the vote with a bounded
- *                 wait (ssa_set_vote_poll_limit); a wave that gives up keeps
- *                 the tile, which is always exact, and the block's count is
+ *                 wait (16384 polls of one LDS word; ssa_set_vote_poll_limit
+ *                 for the debug entry); a wave that gives up keeps the
+ *                 tile, which is always exact, and the block's count is
  *                 then stored as -1 - count, so a negative count flags a
  *                 block whose decisions may differ between its two halves.
  * Inputs o, lse and skip_counts are overwritten; q, k, v are read only.
@@ -277,8 +278,9 @@ int ssa_flow_shift_schedule(double shift, int num_inference_steps, double* t_out
 /* SSA_OK when the current HIP device is gfx950. */
 int ssa_device_check(void);
 
-/* The bound of the wait for the partner's half of the vote, in polls of one
- * LDS word, for every later call of this process (default 16384).  The two
+/* Debug entry only (ssa_fwd_debug): the bound of the wait for the partner's
+ * half of the vote, in polls of one LDS word, for every later call of this
+ * process (default 16384, the constant the other entries use).  The two
  * halves are published in the same phase, so the bound only guards against
  * a wave that never arrives; a test sets it to 0 to drive the give-up path
  * from the host (every tile with the test on is then kept and every count

@@ -379,9 +379,10 @@ def device_check() -> None:
 
 def set_vote_poll_limit(polls: int) -> None:
     """Bound of the wait for the partner wave's half of the vote (polls of
-    one LDS word) for later calls in this process; 16384 by default.  A wave
-    that gives up keeps the tile and its query block's count comes out as
-    -1 - count.  0 forces that path from the host (tests)."""
+    one LDS word) in later fwd_debug calls of this process; 16384 by default,
+    the constant the other entries use.  A wave that gives up keeps the tile
+    and its query block's count comes out as -1 - count.  0 forces that path
+    from the host (tests)."""
     _check(load_library().ssa_set_vote_poll_limit(int(polls)))
 
 

@@ -135,7 +135,7 @@ struct Params {
   float ln_lambda;             // used when lambda_per_seq == 0
   int vote;                    // 0: lambda == 0, nothing is skipped
   int lambda_per_seq;          // 1: ln(lambda_b) = ln(factor / S_b)
-  int spin_limit;              // polls of the partner's half of the vote before the tile is kept
+  int spin_limit;              // debug instance: polls of the partner's half of the vote before the tile is kept
   double factor;
 };
 
@@ -434,6 +434,7 @@ void ssa_fwd_kernel(const Params p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   int nskip = 0;
+  bool timed_out = false;   // this wave gave up waiting for its partner's half of a vote
   uint32_t comp_cur = 0;   // virtual tiles: skip bits of the current 32-tile word
 
   // Scores of the tile between its MFMA and softmax phases.  The softmax
@@ -634,17 +635,22 @@ void ssa_fwd_kernel(const Params p) {
       // against a wave that never arrives.  Each poll is one LDS round trip;
       // sleeping between polls measured slightly slower.  A wave that gives
       // up keeps the tile (always exact) and flags its vote group, whose
-      // skip count is then stored as -1 - count.
+      // skip count is then stored as -1 - count.  The debug instance takes
+      // the bound from the host, so that a test can drive this path; the
+      // product instances keep it a constant (a per-tile flag store, or a
+      // loop bound read from the arguments, measured several percent slower
+      // in skip mode).
       int pv = 0;
       bool got = false;
-      for (int spin = 0; spin < p.spin_limit; ++spin) {
+      const int spin_limit = kDebug ? p.spin_limit : kSpinLimit;
+      for (int spin = 0; spin < spin_limit; ++spin) {
         pv = __hip_atomic_load(&vote_lds[wave ^ 1], kSub, __HIP_MEMORY_SCOPE_WORKGROUP);
         if ((pv >> 1) == kt) {
           got = true;
           break;
         }
       }
-      if (!got && lane == 0) vote_timeout[wave >> 1] = 1;
+      timed_out |= !got;
       skip = vote && own_pass && got && (pv & 1) != 0;
       if constexpr (kDebug) {
         if (lane == 0 && (wave & 1) == 0) {
@@ -710,7 +716,6 @@ void ssa_fwd_kernel(const Params p) {
   // copy into group A's QK^T steps of slot 2j, so it overlaps MFMA work
   // instead of stretching group B's softmax phase.
   if (tid < kWaves) vote_lds[tid] = -2;
-  if (tid < kWaves / 2) vote_timeout[tid] = 0;
   copy_k(0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
@@ -780,6 +785,12 @@ void ssa_fwd_kernel(const Params p) {
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
+
+  // Each vote group's timeout flag, for the epilogue's skip count.
+  if (tid < kWaves / 2) vote_timeout[tid] = 0;
+  __syncthreads();
+  if (timed_out && lane == 0) vote_timeout[wave >> 1] = 1;
+  __syncthreads();
 
   // ---- virtual tiles: add each skipped tile's mean key and value ----
   if constexpr (kComp) {
@@ -911,7 +922,6 @@ void ssa_fwd_kernel(const Params p) {
   }
   const long long nqb_seq = (S_b + kBQ - 1) / kBQ;
   if (p.counts != nullptr && lane == 0 && (wave & 1) == 0 && qb < nqb_seq) {
-    // the last slot's barrier orders the partner's timeout flag before this read
     const int cval = vote_timeout[wave >> 1] != 0 ? -1 - nskip : nskip;
     if (p.cu_seqlens != nullptr) {
       p.counts[(long long)h * qb_total + qb_off + qb] = cval;

@@ -356,11 +356,13 @@ def test_max_prob(ssa, case):
 
 def test_vote_give_up_keeps_every_tile(ssa):
     """The bounded wait for the partner wave's half of the vote, driven from
-    the host: with the poll limit at 0 every wave gives up at once, so every
-    tile is kept (the exact path), every query block's count comes out
-    flagged as -1 - 0, the debug mask shows no skipped tile, and O and LSE
-    equal the dense call's bit for bit (the arithmetic of a kept tile does not
-    depend on the vote).  Restoring the limit restores the normal result."""
+    the host through the debug entry: with the poll limit at 0 every wave
+    gives up at once, so every tile is kept (the exact path), every query
+    block's count comes out flagged as -1 - 0, the mask shows no skipped
+    tile, and O and LSE equal the dense call's bit for bit (the arithmetic of
+    a kept tile does not depend on the vote).  The product entry keeps its
+    constant bound meanwhile, and restoring the limit restores the debug
+    entry's normal result."""
     w = inputs.grid_small(41, (4, 12, 20), heads=2)
     q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
     od, lsed, cd = ssa.fwd(q, k, v, scale=w.scale, factor=0.0)
@@ -370,16 +372,17 @@ def test_vote_give_up_keeps_every_tile(ssa):
     print(f"[case] vote give-up: normal call skips {int(c1.sum())} tiles", flush=True)
     try:
         ssa.set_vote_poll_limit(0)
-        o0, l0, c0 = ssa.fwd(q, k, v, scale=w.scale, threshold=0.05)
         om, lm, cm, mask, _ = ssa.fwd_debug(q, k, v, scale=w.scale, threshold=0.05)
+        o0, l0, c0 = ssa.fwd(q, k, v, scale=w.scale, threshold=0.05)
         torch.cuda.synchronize()
     finally:
         ssa.set_vote_poll_limit(16384)
-    print(f"[case] vote give-up: counts {sorted(set(c0.flatten().tolist()))}, mask skipped {int(mask.sum())}",
-          flush=True)
-    assert (c0 == -1).all() and (cm == -1).all() and int(mask.sum()) == 0
-    assert torch.equal(o0, od) and torch.equal(l0, lsed)
+    print(f"[case] vote give-up: debug counts {sorted(set(cm.flatten().tolist()))}, mask skipped "
+          f"{int(mask.sum())}; product entry skipped {int(c0.sum())}", flush=True)
+    assert (cm == -1).all() and int(mask.sum()) == 0
     assert torch.equal(om, od) and torch.equal(lm, lsed)
-    o2, l2, c2 = ssa.fwd(q, k, v, scale=w.scale, threshold=0.05)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1) and torch.equal(c0, c1)
+    o2, l2, c2, m2, _ = ssa.fwd_debug(q, k, v, scale=w.scale, threshold=0.05)
     torch.cuda.synchronize()
     assert torch.equal(o2, o1) and torch.equal(l2, l1) and torch.equal(c2, c1)
+    assert int(m2.sum()) == int(c1.sum())
