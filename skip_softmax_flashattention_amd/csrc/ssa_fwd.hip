@@ -241,6 +241,10 @@ void ssa_fwd_kernel(const Params p) {
   // contiguous range of the (query group, head, sequence) list: the 32 CUs
   // of an XCD then stream the same head's K/V tiles at the same time and
   // share them in their L2, instead of two heads per XCD at half the reuse.
+  // Within a head the query groups run last to first: keys are visited in
+  // ascending order, so early queries tend to meet their largest scores
+  // early and skip more tiles, and dispatching the costlier late groups
+  // first leaves the cheap ones to fill the end of the launch.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hf = lane >> 5;
   const bool group_b = wave >= 4;
@@ -253,7 +257,7 @@ void ssa_fwd_kernel(const Params p) {
     const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
     const int per = n / kXcds, rem = n % kXcds, xcd = L % kXcds;
     const int W = xcd * per + (xcd < rem ? xcd : rem) + L / kXcds;
-    qg = W % gx;
+    qg = gx - 1 - W % gx;
     h = (W / gx) % gy;
     b = W / (gx * gy);
   } else {
@@ -292,7 +296,7 @@ void ssa_fwd_kernel(const Params p) {
     const int nqg = (S_b + kRowsPerWG - 1) / kRowsPerWG;
     const int item = (int)((long long)p.H * nqg * xcd / kXcds) + local;
     h = item / nqg;
-    qg = item % nqg;
+    qg = nqg - 1 - item % nqg;   // last query group first, as above
   }
   if (qg * kRowsPerWG >= S_b) return;   // whole workgroup past the end of its sequence
 
