@@ -393,9 +393,9 @@ void ssa_fwd_kernel(const Params p) {
     if constexpr (kFp8) copy_block8(kt, dst, blk);
     else copy_block(rk, kt, dst, blk);
   };
-  // The dense instance's copies: instruction j of block blk of tile kt (of V
-  // when is_v, else of K) into the LDS tile at byte offset lds_tile, as in
-  // copy_block but through inline assembly.  The compiler does not see these
+  // The bf16 instances' in-loop copies: instruction j of block blk of tile
+  // kt (of V when is_v, else of K) into the LDS tile at byte offset
+  // lds_tile, as in copy_block but through inline assembly.  The compiler does not see these
   // loads, so it never makes an LDS read of the other buffer wait for them;
   // the vmcnt(0) at the end of every odd slot is their only wait.
   const uint32_t lds_k_off = (uint32_t)(uintptr_t)LDS_PTR(unsigned char, &lds_k[0][0]);
@@ -714,11 +714,12 @@ void ssa_fwd_kernel(const Params p) {
   // softmax phase on odd slots; group B runs what A ran one slot earlier.
   // So on every SIMD one wave feeds the matrix cores while the other runs
   // the softmax.  The MFMA phase of tile j reads K(j) and V(j - 1) in slots
-  // 2j (A) and 2j + 1 (B); group B copies K(j + 1) and V(j), into the other
-  // buffers, at the end of its softmax phase in slot 2j, and every wave waits
-  // for them at the end of slot 2j + 1.  The dense instance moves the V(j)
-  // copy into group A's QK^T steps of slot 2j, so it overlaps MFMA work
-  // instead of stretching group B's softmax phase.
+  // 2j (A) and 2j + 1 (B); group B copies K(j + 1) and V(j) into the other
+  // buffers in slot 2j (at its start in the bf16 instance with the vote, at
+  // the end of its softmax phase in the FP8 one), and every wave waits for
+  // them at the end of slot 2j + 1.  The dense instance moves the V(j) copy
+  // into group A's QK^T steps of slot 2j, so it overlaps MFMA work instead
+  // of stretching group B's softmax phase.
   if (tid < kWaves) vote_lds[tid] = -2;
   copy_k(0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -726,6 +727,29 @@ void ssa_fwd_kernel(const Params p) {
   const int nslots = 2 * nkt + 2;
   for (int slot = 0; slot < nslots; ++slot) {
     const int my = group_b ? slot - 1 : slot;   // this group's own slot counter
+    if constexpr (!kDense && !kFp8) {
+      // Group B's copies of K(j + 1) and V(j), at the start of its even slot
+      // 2j, before its softmax phase.  Untracked, as in the dense instance:
+      // the next slot's MFMA phase reads the other K and V buffers, so it
+      // must not wait for these copies (the compiler, seeing an LDS write,
+      // would make every operand read wait for them); their one wait is the
+      // vmcnt(0) at the end of the odd slot.
+      if (group_b && (slot & 1) == 0) {
+        const int j = slot >> 1;
+          if (j + 1 < nkt) {
+#pragma unroll
+            for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
+              copy_one_untracked(false, j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTileBytes),
+                                 2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
+          }
+          if (j < nkt) {
+#pragma unroll
+            for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
+              copy_one_untracked(true, j, lds_v_off + (uint32_t)((j & 1) * kTileBytes),
+                                 2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
+          }
+      }
+    }
     if (my >= 0) {
       const int kt = my >> 1;
       if ((my & 1) == 0) {
@@ -771,10 +795,12 @@ void ssa_fwd_kernel(const Params p) {
                                2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
         }
       } else {
-        if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
-        if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
-        if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4));
-        if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4) + 1);
+        if constexpr (kFp8) {
+          if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
+          if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
+          if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4));
+          if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4) + 1);
+        }   // the bf16 instance with the vote issues its copies at the start of the slot
       }
     }
     // LDS operations (votes, operand reads) complete before the barrier, so
