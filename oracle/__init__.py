@@ -25,7 +25,9 @@ from .skip_attention import (  # noqa: F401
     skip_attention,
     skip_attention_varlen,
     skip_head,
+    skip_mask_from_row_maxima,
     skipped_mass_head,
+    tile_row_maxima_head,
     max_prob_head,
     virtual_tile_head,
 )

@@ -293,6 +293,71 @@ def prefix_max_margins_head(q: np.ndarray, k: np.ndarray, scale: float,
     return out
 
 
+def tile_row_maxima_head(q: np.ndarray, k: np.ndarray, scale: float, block_k: int = BLOCK_K,
+                         chunk: int = 256) -> np.ndarray:
+    """Step 2 of skip_head for every row and tile of a head at once:
+    tile_max[i, kt] = f32(max over the keys c of tile kt of scale * q_i . k_c),
+    scores in float64, the last tile holding only the keys below S.  Nothing
+    here depends on lambda, so one pass serves the decisions of every lambda
+    (skip_mask_from_row_maxima).  ``chunk`` rows are scored at a time; it only
+    bounds memory.  Returns [S, nKT] float32.
+    """
+    S = q.shape[0]
+    nkt = -(-S // block_k)
+    nfull = S // block_k
+    kT = np.ascontiguousarray(k.T)
+    out = np.empty((S, nkt), dtype=np.float32)
+    for r0 in range(0, S, chunk):
+        s = float(scale) * (q[r0:r0 + chunk] @ kT)                      # [rows, S]
+        out[r0:r0 + chunk, :nfull] = s[:, :nfull * block_k].reshape(s.shape[0], nfull, block_k).max(axis=2)
+        if nfull < nkt:
+            out[r0:r0 + chunk, nfull] = s[:, nfull * block_k:].max(axis=1)
+    return out
+
+
+def skip_mask_from_row_maxima(tile_max: np.ndarray, ln_lambda: Optional[np.float32],
+                              forced_skip: Optional[np.ndarray] = None,
+                              block_q: int = BLOCK_Q):
+    """Steps 3 and 5 of skip_head, reduced to what decides the mask: each row's
+    running maximum m starts at -inf; for each tile in ascending order the
+    row's margin is f32(tile_max) - f32(m) in float32 (+inf on the first
+    tile), the block's margin is the largest over its valid rows, the tile is
+    skipped when that margin is below ln(lambda) in float32, and only a kept
+    tile raises m to max(m, tile_max).  The exponentials and sums do not
+    enter any decision, so the mask and margins equal skip_head's.
+
+    tile_max: [..., S, nKT] float32 from tile_row_maxima_head (leading axes,
+    e.g. heads, are independent problems).  ``forced_skip`` [..., nQB, nKT]
+    replaces the decisions (m then follows the given mask), as in skip_head;
+    ``ln_lambda`` None skips nothing.  Returns (skipped [..., nQB, nKT] bool,
+    margin [..., nQB, nKT] float32).
+    """
+    tile_max = np.asarray(tile_max, dtype=np.float32)
+    lead, (S, nkt) = tile_max.shape[:-2], tile_max.shape[-2:]
+    nqb = -(-S // block_q)
+    tm = np.full(lead + (nqb * block_q, nkt), -np.inf, dtype=np.float32)
+    tm[..., :S, :] = tile_max
+    tm = tm.reshape(lead + (nqb, block_q, nkt))
+    valid = (np.arange(nqb * block_q) < S).reshape(nqb, block_q)
+    m = np.full(lead + (nqb, block_q), -np.inf, dtype=np.float32)
+    skipped = np.zeros(lead + (nqb, nkt), dtype=bool)
+    margin = np.empty(lead + (nqb, nkt), dtype=np.float32)
+    for kt in range(nkt):
+        t = tm[..., kt]
+        with np.errstate(invalid="ignore"):
+            d = np.where(valid, t - m, np.float32(-np.inf))
+        margin[..., kt] = d.max(axis=-1)
+        if forced_skip is not None:
+            skip = np.asarray(forced_skip[..., kt], dtype=bool)
+        elif ln_lambda is None:
+            skip = np.zeros(lead + (nqb,), dtype=bool)
+        else:
+            skip = margin[..., kt] < np.float32(ln_lambda)
+        skipped[..., kt] = skip
+        m = np.where(skip[..., None], m, np.maximum(m, t))
+    return skipped, margin
+
+
 def skipped_mass_head(q: np.ndarray, k: np.ndarray, scale: float, skipped: np.ndarray,
                       block_q: int = BLOCK_Q, block_k: int = BLOCK_K) -> np.ndarray:
     """omega_i: the dense softmax weight that row i puts on keys of its

@@ -154,6 +154,84 @@ def pin_mask_matches_bruteforce_ragged(orc):
         assert (r.skipped == want).all()
 
 
+def _bruteforce_recurrence_mask(q, k, scale, ln_lam, bq, bk, forced=None):
+    """Plain-Python decisions for any lambda: per row a running maximum that
+    only kept tiles raise, the float32 margin against it, a tile skipped when
+    every valid row's margin is below ln_lam (or as ``forced`` says)."""
+    S, D = len(q), len(q[0])
+    nqb, nkt = -(-S // bq), -(-S // bk)
+    mask = [[False] * nkt for _ in range(nqb)]
+    margin = [[0.0] * nkt for _ in range(nqb)]
+    for qb in range(nqb):
+        rows = range(qb * bq, min(S, (qb + 1) * bq))
+        m = {i: -math.inf for i in rows}
+        for kt in range(nkt):
+            keys = range(kt * bk, min(S, (kt + 1) * bk))
+            tmax = {i: max(scale * sum(q[i][t] * k[j][t] for t in range(D)) for j in keys) for i in rows}
+            worst = -math.inf
+            for i in rows:
+                d = math.inf if m[i] == -math.inf else float(np.float32(tmax[i]) - np.float32(m[i]))
+                worst = max(worst, d)
+            margin[qb][kt] = worst
+            skip = bool(forced[qb][kt]) if forced is not None else worst < ln_lam
+            mask[qb][kt] = skip
+            if not skip:
+                for i in rows:
+                    m[i] = max(m[i], tmax[i])
+    return np.array(mask), np.array(margin, dtype=np.float32)
+
+
+def pin_row_maxima_mask_bruteforce(orc):
+    """tile_row_maxima_head + skip_mask_from_row_maxima (the decisions of a
+    whole head from per-row tile maxima) equal plain-Python brute force for
+    lambda below and above 1 (above 1 a skipped tile may hold a row's new
+    maximum, which the running maximum then never sees), with a ragged last
+    query block and key tile, and with a forced mask; and they equal
+    skip_head's decisions and margins on a larger head."""
+    q, k, v = _peaky_head(16, 43, 4)
+    scale = 0.55
+    ql, kl = q.tolist(), k.tolist()
+    tm = orc.tile_row_maxima_head(q, k, scale, block_k=6, chunk=7)
+    assert tm.dtype == np.float32 and tm.shape == (43, 8)
+    for i in (0, 20, 42):
+        for kt in (0, 3, 7):
+            s = [scale * sum(ql[i][t] * kl[j][t] for t in range(4)) for j in range(6 * kt, min(43, 6 * kt + 6))]
+            assert tm[i, kt] == np.float32(max(s))
+    above = 0
+    for lam in (1e-3, 0.2, 1.0, 2.5, 20.0):
+        ln = orc.ln_lambda_f32(lam)
+        want, want_margin = _bruteforce_recurrence_mask(ql, kl, scale, float(ln), 5, 6)
+        got, got_margin = orc.skip_mask_from_row_maxima(tm, ln, block_q=5)
+        assert np.array_equal(got, want), (lam, got.astype(int), want.astype(int))
+        assert np.array_equal(got_margin, want_margin), lam
+        if lam > 1:
+            above += int((want & (want_margin > 0)).sum())   # skipped although a row's maximum rose
+    assert above > 0
+    # ln(lambda) equal to a block's margin: the strict test keeps that tile
+    _, m0 = _bruteforce_recurrence_mask(ql, kl, scale, float(orc.ln_lambda_f32(0.2)), 5, 6)
+    tie = np.float32(np.sort(m0[np.isfinite(m0) & (m0 < 0)])[-1])
+    want, _ = _bruteforce_recurrence_mask(ql, kl, scale, float(tie), 5, 6)
+    got, got_margin = orc.skip_mask_from_row_maxima(tm, tie, block_q=5)
+    assert np.array_equal(got, want) and (~got[got_margin == tie]).all() and (got_margin == tie).any()
+    forced = np.random.default_rng(5).random((9, 8)) < 0.5
+    want, want_margin = _bruteforce_recurrence_mask(ql, kl, scale, 0.0, 5, 6, forced=forced.tolist())
+    got, got_margin = orc.skip_mask_from_row_maxima(tm, None, forced_skip=forced, block_q=5)
+    assert np.array_equal(got, forced) and np.array_equal(got_margin, want_margin)
+    got, _ = orc.skip_mask_from_row_maxima(tm, None, block_q=5)
+    assert not got.any()
+    # a larger head against skip_head, two heads stacked on a leading axis
+    q2, k2, v2 = _peaky_head(17, 300, 16)
+    tms = np.stack([orc.tile_row_maxima_head(q, k, 2.0, block_k=16)
+                    for q, k in ((q2, k2), (k2, q2))])
+    for lam in (0.05, 3.0):
+        ln = orc.ln_lambda_f32(lam)
+        got, got_margin = orc.skip_mask_from_row_maxima(tms, ln, block_q=32)
+        for h, (qh, kh, vh) in enumerate(((q2, k2, v2), (k2, q2, v2))):
+            r = orc.skip_head(qh, kh, vh, 2.0, ln, block_q=32, block_k=16)
+            assert np.array_equal(got[h], r.skipped) and np.array_equal(got_margin[h], r.margin)
+            assert 0 < r.skipped.sum() < r.skipped.size
+
+
 def pin_monotone_in_lambda(orc):
     """For lambda <= 1 a larger lambda skips a superset of tiles."""
     q, k, v = _peaky_head(15, 96, 8)

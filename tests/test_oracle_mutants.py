@@ -76,6 +76,19 @@ MUTANTS = [
      "counts = np.array([block_k for t in range(nkt)], dtype=np.float64)"),
     ("virtual keys double-count kept keys",
      "kept = ~sk[key_tile]", "kept = np.ones(S, dtype=bool)"),
+    ("row maxima: last partial tile dropped",
+     "        if nfull < nkt:\n            out[r0:r0 + chunk, nfull] = s[:, nfull * block_k:].max(axis=1)\n",
+     "        if nfull < nkt:\n            out[r0:r0 + chunk, nfull] = s[:, (nfull - 1) * block_k:].max(axis=1)\n"),
+    ("row maxima without the scale",
+     "s = float(scale) * (q[r0:r0 + chunk] @ kT)", "s = (q[r0:r0 + chunk] @ kT)"),
+    ("row-maxima recurrence: skipped tiles raise m",
+     "m = np.where(skip[..., None], m, np.maximum(m, t))", "m = np.maximum(m, t)"),
+    ("row-maxima recurrence: padding rows vote",
+     "d = np.where(valid, t - m, np.float32(-np.inf))", "d = t - m"),
+    ("row-maxima recurrence: vote on any row",
+     "margin[..., kt] = d.max(axis=-1)", "margin[..., kt] = d.min(axis=-1)"),
+    ("row-maxima recurrence: non-strict comparison",
+     "skip = margin[..., kt] < np.float32(ln_lambda)", "skip = margin[..., kt] <= np.float32(ln_lambda)"),
     ("lambda for a fraction one step too low",
      "ln_lam = float(np.nextafter(np.float32(edge), np.float32(np.inf)))", "ln_lam = float(np.float32(edge))"),
     ("lambda for a fraction with the count rounded down",
