@@ -69,12 +69,14 @@ def compare_head_blocks(qd, kd, vd, scale, ln_lambda, qblocks, gpu_mask, gpu_o, 
                   o_max=float(err.max()), o_mean=float(err.mean()), lse_max=float(lerr.max()))
 
 
-def whole_head_mask_closed_form(gpu_mask, margins, ln_lambda):
-    """Every tile of a head, lambda <= 1: the GPU's decisions [nQB, nKT]
-    against the closed form margin < ln(lambda) with the dense prefix-maximum
-    margins (oracle.prefix_max_margins_head).  Tiles within MASK_BAND of
-    ln(lambda) may differ; everything else must be identical.  Returns
-    (tiles compared exactly, tiles exempt and different)."""
+def whole_mask_forced(gpu_mask, margins, ln_lambda):
+    """Every tile of one or more heads: the GPU's decisions [..., nQB, nKT]
+    against the oracle's margins computed along the GPU's own decisions
+    (oracle.skip_mask_from_row_maxima with forced_skip = the GPU's mask), so
+    a tile inside MASK_BAND that went the other way cannot move the two
+    running maxima apart.  Outside the band every decision must be
+    margin < ln(lambda).  Returns (tiles compared exactly, tiles inside the
+    band that differ)."""
     want = margins < np.float32(ln_lambda)
     band = np.abs(margins.astype(np.float64) - float(ln_lambda)) <= MASK_BAND
     diff = gpu_mask != want
