@@ -335,15 +335,15 @@ def skip_mask_from_row_maxima(tile_max: np.ndarray, ln_lambda: Optional[np.float
     tile_max = np.asarray(tile_max, dtype=np.float32)
     lead, (S, nkt) = tile_max.shape[:-2], tile_max.shape[-2:]
     nqb = -(-S // block_q)
-    tm = np.full(lead + (nqb * block_q, nkt), -np.inf, dtype=np.float32)
-    tm[..., :S, :] = tile_max
-    tm = tm.reshape(lead + (nqb, block_q, nkt))
+    tm = np.full((nkt,) + lead + (nqb * block_q,), -np.inf, dtype=np.float32)   # tile-major
+    tm[..., :S] = np.moveaxis(tile_max, -1, 0)
+    tm = tm.reshape((nkt,) + lead + (nqb, block_q))
     valid = (np.arange(nqb * block_q) < S).reshape(nqb, block_q)
     m = np.full(lead + (nqb, block_q), -np.inf, dtype=np.float32)
     skipped = np.zeros(lead + (nqb, nkt), dtype=bool)
     margin = np.empty(lead + (nqb, nkt), dtype=np.float32)
     for kt in range(nkt):
-        t = tm[..., kt]
+        t = tm[kt]
         with np.errstate(invalid="ignore"):
             d = np.where(valid, t - m, np.float32(-np.inf))
         margin[..., kt] = d.max(axis=-1)
