@@ -736,18 +736,18 @@ void ssa_fwd_kernel(const Params p) {
       // vmcnt(0) at the end of the odd slot.
       if (group_b && (slot & 1) == 0) {
         const int j = slot >> 1;
-          if (j + 1 < nkt) {
+        if (j + 1 < nkt) {
 #pragma unroll
-            for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
-              copy_one_untracked(false, j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTileBytes),
-                                 2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
-          }
-          if (j < nkt) {
+          for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
+            copy_one_untracked(false, j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTileBytes),
+                               2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
+        }
+        if (j < nkt) {
 #pragma unroll
-            for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
-              copy_one_untracked(true, j, lds_v_off + (uint32_t)((j & 1) * kTileBytes),
-                                 2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
-          }
+          for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
+            copy_one_untracked(true, j, lds_v_off + (uint32_t)((j & 1) * kTileBytes),
+                               2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
+        }
       }
     }
     if (my >= 0) {
