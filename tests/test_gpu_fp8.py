@@ -11,13 +11,17 @@ here is EPS = 2^-10 of that sum, per score (oracle.fp8.score_error_bound):
     bound of the block's rows (the margin is a difference of two scores);
   * O: against the oracle forced to the GPU's mask, the bars of tests/parity.py;
   * LSE: within 1e-3 plus twice the row's bound.
+At full size (Wan-like, long sequence) the quantiser and the tile mask are
+checked over the whole problem, O and LSE on sampled query blocks.
 """
 import json
 import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import oracle
 from oracle import fp8 as ofp8
@@ -201,21 +205,55 @@ def test_fp8_lambda_above_one(ssa):
     _check_attention(ssa, w, "fp8 lambda > 1", threshold=3.0)
 
 
-def test_fp8_wan_like_sampled(ssa):
-    """The full Wan-like problem: sampled tokens and tiles of the quantiser,
-    sampled query blocks of the attention, and the FP8 output's distance to
-    the bf16 path's (reported)."""
+def _whole_fp8(ssa, w, name, mask, ln):
+    """The whole problem (B = 1): the quantiser's codes and scales of every
+    head bit for bit, and every tile decision against the oracle's decision
+    recurrence on the dequantised operands (oracle.tile_row_maxima_head,
+    oracle.skip_mask_from_row_maxima driven by the kernel's mask).  The band
+    of a block is 1e-3 plus twice the largest bound of its rows, each row's
+    bound taken with Cauchy-Schwarz, |decode(q_i)| |decode(k_c)| >=
+    sum_d |decode(q_id)| |decode(k_cd)|, so it is never below the one the
+    sampled checks use (oracle.fp8.score_error_bound)."""
+    q8, k8, qs, ks = (t.cpu().numpy() for t in ssa.quantize_qk_fp8(w.q.cuda(), w.k.cuda()))
+    H, S = w.q.shape[1], w.q.shape[2]
+    nqb = -(-S // 64)
+
+    def head(h):
+        ops = ofp8.quantize_head(oracle.from_bf16(w.q[0, h]), oracle.from_bf16(w.k[0, h]))
+        same = bool((q8[0, h] == ops.q_codes).all() and (k8[0, h] == ops.k_codes).all()
+                    and (qs[0, h] == ops.q_scale).all() and (ks[0, h] == ops.k_scale).all())
+        tm = oracle.tile_row_maxima_head(ops.q, ops.k, w.scale)
+        _, margins = oracle.skip_mask_from_row_maxima(tm, ln, forced_skip=mask[0, h])
+        nq = np.linalg.norm(ofp8.e4m3_decode(ops.q_codes), axis=1) * ops.q_scale.astype(np.float64)
+        nk = np.linalg.norm(ofp8.e4m3_decode(ops.k_codes), axis=1) * ops.k_scale[np.arange(S) // 128]
+        bound = np.zeros(nqb * 64)
+        bound[:S] = EPS * w.scale * nq * nk.max()
+        band = 1e-3 + 2 * bound.reshape(nqb, 64).max(axis=1)[:, None]
+        near = np.abs(margins.astype(np.float64) - float(ln)) <= band
+        diff = mask[0, h] != (margins < np.float32(ln))
+        return same, int((diff & ~near).sum()), int((diff & near).sum()), int((~near).sum()), float(band.max())
+
+    with threadpool_limits(1), ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        res = list(ex.map(head, range(H)))
+    print(f"[whole fp8] {name}: {H} heads: quantiser {'equal' if all(r[0] for r in res) else 'DIFFERS'}; "
+          f"{sum(r[3] for r in res)} tiles outside the band, {sum(r[1] for r in res)} of them different; "
+          f"{sum(r[2] for r in res)} inside the band different; widest band {max(r[4] for r in res):.2e}", flush=True)
+    assert all(r[0] for r in res), [h for h, r in enumerate(res) if not r[0]]
+    assert sum(r[1] for r in res) == 0
+
+
+def test_fp8_wan_like(ssa):
+    """The full Wan-like problem: the quantiser and the tile mask over the
+    whole problem, sampled query blocks of the attention's O and LSE, and the
+    FP8 output's distance to the bf16 path's (reported)."""
     w = inputs.wan()
     S = w.q.shape[2]
     rng = np.random.default_rng(25)
-    rows = np.sort(rng.choice(S, 2000, replace=False))
-    tiles = np.sort(rng.choice(-(-S // 128), 24, replace=False))
-    tiles[-1] = -(-S // 128) - 1
-    _check_quant(ssa, w, heads=[(0, 0), (0, 21), (0, 39)], rows=rows, tiles=tiles)
     lam = json.load(open(os.path.join(GOLDEN, "wan_lambdas.json")))["lambda"]["0.75"]
     qbs = np.sort(rng.choice(-(-S // 64), 5, replace=False))
     qbs[-1] = -(-S // 64) - 1
-    _check_attention(ssa, w, "fp8 wan-like", qblocks=qbs, heads=[(0, 0), (0, 39)], factor=lam * S)
+    mask = _check_attention(ssa, w, "fp8 wan-like", qblocks=qbs, heads=[(0, 0), (0, 39)], factor=lam * S)
+    _whole_fp8(ssa, w, "wan-like", mask, oracle.ln_lambda_f32(oracle.resolve_lambda(factor=lam * S, seqlen=S)))
     q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
     q8, k8, qs, ks = ssa.quantize_qk_fp8(q, k)
     o8, _, c8 = ssa.fwd_fp8(q8, k8, qs, ks, v, scale=w.scale, factor=lam * S)
@@ -228,19 +266,17 @@ def test_fp8_wan_like_sampled(ssa):
           flush=True)
 
 
-def test_fp8_long_sampled(ssa):
-    """Long-sequence workload (S = 36864, H = 24, 2% sink keys scaled x4): the
-    quantiser on sampled tokens and tiles, the attention on sampled blocks at
-    threshold 1e-3."""
+def test_fp8_long(ssa):
+    """Long-sequence workload (S = 36864, H = 24, 2% sink keys scaled x4) at
+    threshold 1e-3: the quantiser and the tile mask over the whole problem,
+    O and LSE on sampled blocks."""
     w = inputs.long_seq()
     S = w.q.shape[2]
     rng = np.random.default_rng(26)
-    rows = np.sort(rng.choice(S, 2000, replace=False))
-    tiles = np.sort(rng.choice(-(-S // 128), 24, replace=False))
-    _check_quant(ssa, w, heads=[(0, 0), (0, 23)], rows=rows, tiles=tiles)
     qbs = np.sort(rng.choice(-(-S // 64), 5, replace=False))
     qbs[-1] = -(-S // 64) - 1
-    _check_attention(ssa, w, "fp8 long", qblocks=qbs, heads=[(0, 0), (0, 23)], threshold=1e-3)
+    mask = _check_attention(ssa, w, "fp8 long", qblocks=qbs, heads=[(0, 0), (0, 23)], threshold=1e-3)
+    _whole_fp8(ssa, w, "long", mask, oracle.ln_lambda_f32(1e-3))
 
 
 def _batched(seed):
