@@ -26,8 +26,10 @@ same inputs), and the traced mean duration of each kernel instance goes
 into ``rocprof``; ``roofline`` is computed from the traced skip kernel.  The
 timed loop itself is bracketed by HIP events on the launch stream
 (``skip_step``, ``dense_step``, ``ms_per_step``, and ``roofline.achieved_events``).
+``energy`` holds the socket power (hwmon, read-only) over back-to-back dense
+and skip calls after the timed loop, and each call's energy.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15] [--no-trace]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-seconds 15] [--no-trace] [--energy-calls 150]
     python bench.py --power 200      # socket power and energy per call instead
 """
 from __future__ import annotations
@@ -217,37 +219,59 @@ def copy_reference(launches):
     print(json.dumps({"counters_run": "copy", "bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}), flush=True)
 
 
-def power_run(ssa, q, k, v, scale, factor, calls):
+def _power_file():
+    import glob
+    files = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+    return files[0] if files else None
+
+
+def _read_w(path):
+    with open(path) as f:
+        return float(f.read()) / 1e6
+
+
+def idle_power(quiet=2.0, seconds=1.0):
+    """Socket power with no kernel running: the mean of 20 ms samples over
+    ``seconds`` after ``quiet`` seconds of rest (the board stays above idle
+    for a while after heavy work).  None where the sensor cannot be read."""
+    path = _power_file()
+    if path is None:
+        return None
+    time.sleep(quiet)
+    t_end, vals = time.time() + seconds, []
+    while time.time() < t_end:
+        vals.append(_read_w(path))
+        time.sleep(0.02)
+    return round(sum(vals) / len(vals), 1)
+
+
+def power_run(ssa, q, k, v, scale, factor, calls, idle_w=None):
     """Socket power while the dense and the skip calls each run back to back.
 
     Reads the GPU's hwmon power1_input (and power1_cap) every 20 ms from a
-    host thread; nothing is written.  Returns a dict, or None where the
-    files cannot be read."""
-    import glob
+    host thread; nothing is written.  ``idle_w`` is measured first (1 s)
+    unless given.  Returns a dict, or None where the files cannot be read."""
     import threading
     import numpy as np
     import torch
-    files = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
-    if not files:
+    path = _power_file()
+    if path is None:
         return None
-
-    def read(path):
-        with open(path) as f:
-            return float(f.read())
     try:
-        cap = read(files[0].replace("power1_input", "power1_cap")) / 1e6
+        cap = _read_w(path.replace("power1_input", "power1_cap"))
     except OSError:
         cap = None
     samples, stop = [], threading.Event()
 
     def sampler():
         while not stop.is_set():
-            samples.append((time.time(), read(files[0]) / 1e6))
+            samples.append((time.time(), _read_w(path)))
             time.sleep(0.02)
+    if idle_w is None:
+        idle_w = idle_power(quiet=0.0)
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
-    time.sleep(1.0)
-    out = {"cap_w": cap, "idle_w": round(float(np.mean([w for _, w in samples])), 1)}
+    out = {"cap_w": cap, "idle_w": idle_w}
     for name, f in (("dense", 0.0), ("skip", factor)):
         for _ in range(10):
             ssa.fwd(q, k, v, factor=f, scale=scale)
@@ -281,6 +305,8 @@ def main():
                     help="launch only one configuration (or the plain copy reference), for rocprofv3 --pmc; "
                          "'trace' launches the dense and skip calls interleaved, for the kernel trace")
     ap.add_argument("--no-trace", action="store_true", help="skip the rocprofv3 kernel-trace child run")
+    ap.add_argument("--energy-calls", type=int, default=150,
+                    help="back-to-back dense and skip calls for the energy figures of the benchmark line (0: none)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -314,6 +340,8 @@ def main():
     B, H, S, D = q.shape
     factor = lam * S
     dense_flops = 4.0 * B * H * S * S * D
+    # idle power for the energy figures, before this process runs any kernel
+    idle_w = idle_power() if args.counters is None and args.power == 0 and args.energy_calls > 0 else None
 
     if args.power > 0:
         print(json.dumps({"power_run": power_run(ssa, q, k, v, w.scale, factor, args.power),
@@ -519,6 +547,23 @@ def main():
     others["varlen_workload"] = f"H={qv.shape[1]} S_b={lens}, calibrated a={cal['a']:.5f} b={cal['b']:.4f}, seed 4"
     del qv, kv, vv, wv
 
+    # Socket power and energy per call of the timed dense and skip calls, and
+    # the energy above idle that each call's work takes (E - P_idle t): while
+    # both settle at the same power, their time ratio follows that energy ratio.
+    energy = None
+    if args.energy_calls > 0:
+        energy = power_run(ssa, q, k, v, w.scale, factor, args.energy_calls, idle_w=idle_w)
+        if energy is not None:
+            p_i = energy["idle_w"]
+            work = {n: energy[n]["energy_j_per_call"] - p_i * energy[n]["ms_per_call"] * 1e-3
+                    for n in ("dense", "skip")}
+            energy["work_energy_j"] = {n: round(x, 2) for n, x in work.items()}
+            # time ratio = work-energy ratio x ratio of the power above idle each call holds
+            energy["work_energy_ratio"] = round(work["dense"] / work["skip"], 4)
+            energy["power_above_idle_ratio"] = round((energy["skip"]["power_w"] - p_i)
+                                                     / (energy["dense"]["power_w"] - p_i), 4)
+            energy["calls"] = args.energy_calls
+
     # Roofline of the skip kernel: executed FLOP over its traced mean duration
     # (rocprofv3), else over the HIP-event mean of the timed loop.
     t_trace_s = t_trace_d = None
@@ -608,6 +653,7 @@ def main():
                            "dense_mfma_util": round(dense_flops / 8 / (d5 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "speedup_vs_dense": round(d5 / s5, 4)},
         "other_configs": others,
+        "energy": energy,
         "timed_wall_s": round(t_wall, 3),
         "kernel_sha256_16": kernel_hash(),
     }

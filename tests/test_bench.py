@@ -45,7 +45,7 @@ def test_issued_mfma_flops_pads_tiles():
 def test_bench_json_line():
     """A short run prints one JSON line with every field the driver reads."""
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
-                        "--cpu-seconds", "1"], capture_output=True, text=True, timeout=280, cwd=ROOT)
+                        "--cpu-seconds", "1", "--energy-calls", "40"], capture_output=True, text=True, timeout=280, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     d = json.loads(r.stdout.strip().splitlines()[-1])
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
@@ -74,6 +74,14 @@ def test_bench_json_line():
     assert tr is not None and roof["timing"] == "rocprofv3 kernel trace"
     assert tr["kernels"][bench.KERNEL_SKIP]["calls"] == 3 and tr["kernels"][bench.KERNEL_DENSE]["calls"] == 3
     assert roof["kernel_ms"] == tr["skip_kernel_mean_ms"] <= 1.05 * d["ms_per_step"]
+    # energy figures where the board's power sensor can be read
+    en = d["energy"]
+    if en is not None:
+        assert en["idle_w"] > 0 and en["dense"]["power_w"] > en["idle_w"] and en["skip"]["power_w"] > en["idle_w"]
+        assert en["work_energy_ratio"] > 1.0 and en["power_above_idle_ratio"] > 0.0
+        # the time ratio of the two calls is the product of the two ratios
+        t_ratio = en["dense"]["ms_per_call"] / en["skip"]["ms_per_call"]
+        assert abs(en["work_energy_ratio"] * en["power_above_idle_ratio"] - t_ratio) < 0.01 * t_ratio
 
 
 @pytest.mark.gpu
