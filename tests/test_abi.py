@@ -145,6 +145,28 @@ def test_virtual_argument_errors(lib):
     assert call(p0=-1.0) == BAD_THRESHOLD
 
 
+def test_virtual_noalloc_refuses_before_any_hip_call(lib):
+    """The static-workspace entry refuses, on the host, calls whose tile means
+    need more than SSA_VIRTUAL_NOALLOC_BYTES (B x H x ceil(S/128) above
+    16 MiB / 768 = 21,845 tiles), and validates like fwd_virtual."""
+    fn = lib.ssa_fwd_virtual_noalloc
+    fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int] + \
+        [ctypes.c_double] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    limit = (16 << 20) // (3 * 128 * 2)
+    assert limit == 21845
+
+    def call(B=1, H=2, S=256, p0=1.0):
+        return fn(FAKE, FAKE, FAKE, FAKE, None, B, H, S, 128, 0.088, 0, p0, 0.0, 0.0, S, None, None)
+    assert call(H=limit + 1, S=128) == UNSUPPORTED
+    assert "static workspace" in lib.ssa_last_error().decode()
+    assert call(B=11, H=1, S=2048 * 128) == UNSUPPORTED         # 22,528 tiles
+    assert call(p0=-1.0) == BAD_THRESHOLD
+    assert fn(None, FAKE, FAKE, FAKE, None, 1, 2, 256, 128, 0.088, 0, 1.0, 0.0, 0.0, 256, None, None) == INVALID
+    # within the limit the call gets as far as the device (none here)
+    assert call(H=limit, S=128) == DEVICE
+
+
 def test_fp8_argument_errors(lib):
     def quant(q=FAKE, q8=FAKE, D=128, S=256):
         return lib.ssa_quantize_qk_fp8(q, FAKE, q8, FAKE, FAKE, FAKE, 1, 2, S, D, None)
