@@ -43,11 +43,11 @@ def test_tiny_vs_fp32_oracle(ssa, factor):
     _run(ssa, inputs.tiny(), f"tiny fp32-oracle factor={factor}", factor=factor, ref=c_oracle.oracle().skip_head)
 
 
-@pytest.mark.parametrize("lam", [1e-4, 1e-2])
+@pytest.mark.parametrize("lam", [1e-4, 1e-3, 1e-2, 0.3])
 def test_mid_vs_fp32_oracle(ssa, lam):
+    """Every head of the Mid workload (B = 2, H = 8)."""
     from oracle import c_oracle
-    _run(ssa, inputs.mid(), f"mid fp32-oracle lambda={lam}", threshold=lam, heads=[(0, 0), (1, 7)],
-         ref=c_oracle.oracle().skip_head)
+    _run(ssa, inputs.mid(), f"mid fp32-oracle lambda={lam}", threshold=lam, ref=c_oracle.oracle().skip_head)
 
 
 def test_wan_like_sampled_vs_fp32_oracle(ssa):
@@ -194,10 +194,15 @@ def test_lambda_above_one(ssa):
 
 
 # ---- Mid workload: B=2, H=8, S=4096, k = q ----------------------------------------------
-@pytest.mark.parametrize("lam", [1e-4, 1e-3, 1e-2])
+# At scale 1/sqrt(128) every later tile's maximum of this problem lies within
+# about 2.5 of the running maximum, so the thresholds 1e-4 .. 1e-2 keep every
+# tile (the mask is still compared, all kept); 0.1 and 0.3 skip some.
+@pytest.mark.parametrize("lam", [1e-4, 1e-3, 1e-2, 0.1, 0.3])
 def test_mid(ssa, lam):
     w = inputs.mid()
-    _run(ssa, w, "mid", threshold=lam)
+    rep = _run(ssa, w, "mid", threshold=lam)
+    if lam >= 0.1:
+        assert rep.skipped > 0
 
 
 # ---- packed variable-length batches ---------------------------------------------------
