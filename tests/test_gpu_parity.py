@@ -37,7 +37,7 @@ def _run(ssa, w, name, **kw):
 # ---- Against the single-precision C oracle ---------------------------------
 # The same bar, with the reference recurrence run in float32 by the plain-C
 # oracle (oracle/skip_attention_c.c) instead of the float64 Python one.
-@pytest.mark.parametrize("factor", [0.0, 0.5, 4.0])
+@pytest.mark.parametrize("factor", [0.0, 0.5, 4.0, 20480.0])
 def test_tiny_vs_fp32_oracle(ssa, factor):
     from oracle import c_oracle
     _run(ssa, inputs.tiny(), f"tiny fp32-oracle factor={factor}", factor=factor, ref=c_oracle.oracle().skip_head)
@@ -67,12 +67,18 @@ def test_wan_like_sampled_vs_fp32_oracle(ssa):
 
 
 # ---- Tiny workload: B=1, H=2, S=1024; factor in {0, 0.5, 4.0} ----------------
-@pytest.mark.parametrize("factor", [0.0, 0.5, 4.0])
+# With i.i.d. scores every tile's maximum is close to the running maximum:
+# factors 0.5 and 4 (lambda = 0.5/1024, 4/1024) keep every tile.  Skipping
+# starts near lambda = 5; factor 20480 (lambda = 20, where kept tiles can
+# raise the running maximum after skipped ones) skips about a quarter.
+@pytest.mark.parametrize("factor", [0.0, 0.5, 4.0, 20480.0])
 def test_tiny(ssa, factor):
     w = inputs.tiny()
     rep = _run(ssa, w, "tiny", factor=factor)
     if factor == 0.0:
         assert rep.skipped == 0
+    if factor > 1024:
+        assert rep.skipped > 0
 
 
 def test_tiny_dense_matches_dense_oracle(ssa):
