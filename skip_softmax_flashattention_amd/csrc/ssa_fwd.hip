@@ -25,7 +25,8 @@
 // Group B runs one slot behind group A, so in every slot one wave of each
 // SIMD feeds the matrix cores while the other runs the softmax.  A call
 // without the skip test (lambda = 0) runs a separate instance of the kernel
-// whose only difference is which wave issues the V copies, and when.
+// without the vote, whose group A issues the V copies inside its QK^T steps
+// (group B still issues the K copies, after its softmax phase).
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  S^T is
 // 4 key blocks of 32 x 32: a lane holds one query row and 16 keys per block,
@@ -716,10 +717,10 @@ void ssa_fwd_kernel(const Params p) {
   // the softmax.  The MFMA phase of tile j reads K(j) and V(j - 1) in slots
   // 2j (A) and 2j + 1 (B); group B copies K(j + 1) and V(j) into the other
   // buffers in slot 2j (at its start in the bf16 instance with the vote, at
-  // the end of its softmax phase in the FP8 one), and every wave waits for
-  // them at the end of slot 2j + 1.  The dense instance moves the V(j) copy
-  // into group A's QK^T steps of slot 2j, so it overlaps MFMA work instead
-  // of stretching group B's softmax phase.
+  // the end of its softmax phase in the FP8 and dense ones), and every wave
+  // waits for them at the end of slot 2j + 1.  The dense instance moves the
+  // V(j) copy into group A's QK^T steps of slot 2j, so it overlaps MFMA work
+  // instead of stretching group B's softmax phase.
   if (tid < kWaves) vote_lds[tid] = -2;
   copy_k(0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
