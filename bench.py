@@ -50,10 +50,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak (published)
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E bandwidth (published)
 METRIC = "effective TFLOP/s + MFMA util at S=32760 H=40 D=128, and speedup vs λ=0 at ~75% skip"
 KERNEL_SRC = os.path.join(ROOT, "skip_softmax_flashattention_amd", "csrc", "ssa_fwd.hip")
 KERNEL_DENSE = "ssa_fwd_kernel<false, false, false, true>"    # the lambda = 0 instance
 KERNEL_SKIP = "ssa_fwd_kernel<false, false, false, false>"    # the instance with the skip test
+KERNEL_FP8 = "ssa_fwd_kernel<false, false, true, false>"      # FP8 scores
+KERNEL_VIRTUAL = "ssa_fwd_kernel<false, true, false, false>"  # virtual tiles for skipped tiles
+SIDE_KERNELS = ("tile_means_kernel", "quant_q_kernel", "quant_k_kernel")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_wan_like.json")
 
 
@@ -95,8 +100,9 @@ def cpu_model() -> str:
 
 def rocprof_trace(steps, warmup, timeout=600):
     """Run this script under rocprofv3 --kernel-trace --stats (the dense and
-    skip calls of the headline workload, interleaved) and return the traced
-    mean duration of each ssa_fwd_kernel instance, or None when rocprofv3 is
+    skip calls of the headline workload, interleaved, then the FP8-score and
+    virtual-tile calls) and return the traced mean duration of each
+    ssa_fwd_kernel instance and side kernel, or None when rocprofv3 is
     missing or wrote no statistics.  rocprofv3 can end with a segmentation
     fault after the program and its files are complete; the statistics are
     used whenever they were written."""
@@ -118,8 +124,12 @@ def rocprof_trace(steps, warmup, timeout=600):
         with open(stats) as f:
             for row in csv.DictReader(f):
                 name = row["Name"]
+                key = None
                 if "ssa_fwd_kernel<" in name:
                     key = "ssa_fwd_kernel<" + name.split("ssa_fwd_kernel<", 1)[1].split(">", 1)[0] + ">"
+                else:
+                    key = next((k_ for k_ in SIDE_KERNELS if k_ + "(" in name or name.endswith(k_)), None)
+                if key is not None:
                     kernels[key] = {"calls": int(row["Calls"]), "mean_ms": float(row["AverageNs"]) / 1e6,
                                     "min_ms": float(row["MinNs"]) / 1e6, "max_ms": float(row["MaxNs"]) / 1e6}
         return {"command": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o bench -- python3 bench.py "
@@ -355,7 +365,15 @@ def main():
             ssa.fwd(q, k, v, factor=0.0, scale=w.scale)
             ssa.fwd(q, k, v, factor=factor, scale=w.scale)
         torch.cuda.synchronize()
-        print(json.dumps({"counters_run": "trace", "launches": 2 * (args.warmup + args.steps),
+        # Then the two variants at the same lambda: quantisation + FP8-score
+        # call, and the virtual-tile call (tile-mean pre-pass + its kernel).
+        ws = torch.empty(ssa.virtual_workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup + args.steps):
+            q8, k8, qs8, ks8 = ssa.quantize_qk_fp8(q, k)
+            ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=factor, scale=w.scale)
+            ssa.fwd_virtual(q, k, v, factor=factor, scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": "trace", "launches": 7 * (args.warmup + args.steps),
                           "kernel_sha256_16": kernel_hash()}), flush=True)
         return
 
@@ -457,7 +475,9 @@ def main():
     # FP8-score kernel at lambda = 0 and at the timed lambda, interleaved with
     # the bf16 dense call; the FP8 call's own skip fraction at that lambda.
     q8, k8, qs8, ks8 = ssa.quantize_qk_fp8(q, k)
-    _, _, c8 = ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=factor, scale=w.scale)
+    _, _, c8, mask8, _ = ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=factor, scale=w.scale, debug=True)
+    mask8_np = mask8.cpu().numpy().astype(bool)
+    del mask8
     ssa.fwd_fp8(q8, k8, qs8, ks8, v, factor=0.0, scale=w.scale)
     torch.cuda.synchronize()
     n8 = max(5, args.steps // 4)
@@ -588,6 +608,42 @@ def main():
         rocprof["kernels"] = {k_: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v_.items()}
                               for k_, v_ in rocprof["kernels"].items()}
 
+    # The variants' kernels against their own rooflines, from the same trace:
+    # the FP8-score kernel against the peak of its FLOP mix (QK^T on fp8,
+    # P.V on bf16), the quantiser and the tile-mean pre-pass against HBM.
+    variants = None
+    if trace is not None:
+        ks = trace["kernels"]
+        variants = {}
+        if KERNEL_FP8 in ks:
+            t = ks[KERNEL_FP8]["mean_ms"] * 1e-3
+            qk8 = dense_flops / 2.0
+            pv8 = executed_flops(mask8_np, S) - qk8
+            t_bound = qk8 / (PEAK_FP8_TFLOPS * 1e12) + pv8 / (PEAK_BF16_TFLOPS * 1e12)
+            variants["fp8_scores_kernel"] = {
+                "kernel": KERNEL_FP8, "bound": "mfma", "kernel_ms": round(t * 1e3, 4),
+                "qk_fp8_tflop": round(qk8 / 1e12, 4), "pv_bf16_tflop": round(pv8 / 1e12, 4),
+                "achieved": round((qk8 + pv8) / t / 1e12, 2), "peak": round((qk8 + pv8) / t_bound / 1e12, 2),
+                "unit": "TFLOP/s", "frac": round(t_bound / t, 4)}
+        if all(k_ in ks for k_ in ("quant_q_kernel", "quant_k_kernel")):
+            t = (ks["quant_q_kernel"]["mean_ms"] + ks["quant_k_kernel"]["mean_ms"]) * 1e-3
+            by = 2 * B * H * S * D * 2 + 2 * B * H * S * D + 4 * B * H * S + 4 * B * H * -(-S // 128)
+            variants["fp8_quantize"] = {"kernels": ["quant_q_kernel", "quant_k_kernel"], "bound": "hbm",
+                                        "kernel_ms": round(t * 1e3, 4), "bytes": by,
+                                        "achieved": round(by / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                        "frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+        if "tile_means_kernel" in ks:
+            t = ks["tile_means_kernel"]["mean_ms"] * 1e-3
+            by = 2 * B * H * S * D * 2 + B * H * -(-S // 128) * 3 * D * 2
+            variants["virtual_tile_means"] = {"kernel": "tile_means_kernel", "bound": "hbm",
+                                              "kernel_ms": round(t * 1e3, 4), "bytes": by,
+                                              "achieved": round(by / t / 1e9, 1), "peak": PEAK_HBM_GBS,
+                                              "unit": "GB/s", "frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+        if KERNEL_VIRTUAL in ks and KERNEL_SKIP in ks:
+            t = ks[KERNEL_VIRTUAL]["mean_ms"]
+            variants["virtual_tiles_kernel"] = {"kernel": KERNEL_VIRTUAL, "kernel_ms": round(t, 4),
+                                                "over_plain_skip_kernel": round(t / ks[KERNEL_SKIP]["mean_ms"] - 1, 4)}
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -627,6 +683,7 @@ def main():
             "frac_events": round(exe / PEAK_BF16_TFLOPS, 4),
         },
         "rocprof": rocprof,
+        "variant_rooflines": variants,
         "skip_step": {
             "ms_mean": round(t_s, 4), "ms_min": round(float(ms_skip.min()), 4),
             "ms_median": round(float(np.median(ms_skip)), 4),

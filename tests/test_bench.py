@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PEAK_MIX = (2500.0, 5000.0)   # a mix of fp8 and bf16 MFMA FLOP has a peak between the two
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
@@ -74,6 +75,15 @@ def test_bench_json_line():
     assert tr is not None and roof["timing"] == "rocprofv3 kernel trace"
     assert tr["kernels"][bench.KERNEL_SKIP]["calls"] == 3 and tr["kernels"][bench.KERNEL_DENSE]["calls"] == 3
     assert roof["kernel_ms"] == tr["skip_kernel_mean_ms"] <= 1.05 * d["ms_per_step"]
+    # the variants' kernels against their own rooflines, from the same trace
+    var = d["variant_rooflines"]
+    for key in ("fp8_scores_kernel", "fp8_quantize", "virtual_tile_means", "virtual_tiles_kernel"):
+        assert key in var and var[key]["kernel_ms"] > 0, key
+    for key in ("fp8_scores_kernel", "fp8_quantize", "virtual_tile_means"):
+        assert 0.0 < var[key]["frac"] < 1.0, (key, var[key])
+    f8 = var["fp8_scores_kernel"]
+    assert PEAK_MIX[0] <= f8["peak"] <= PEAK_MIX[1]
+    assert tr["kernels"][bench.KERNEL_FP8]["calls"] == 3
     # energy figures where the board's power sensor can be read
     en = d["energy"]
     if en is not None:
