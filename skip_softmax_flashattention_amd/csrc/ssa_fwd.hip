@@ -394,9 +394,9 @@ void ssa_fwd_kernel(const Params p) {
     if constexpr (kFp8) copy_block8(kt, dst, blk);
     else copy_block(rk, kt, dst, blk);
   };
-  // The bf16 instances' in-loop copies: instruction j of block blk of tile
-  // kt (of V when is_v, else of K) into the LDS tile at byte offset
-  // lds_tile, as in copy_block but through inline assembly.  The compiler does not see these
+  // The in-loop copies: instruction j of block blk of tile kt (of V when
+  // is_v, else of bf16 K) into the LDS tile at byte offset lds_tile, as in
+  // copy_block but through inline assembly.  The compiler does not see these
   // loads, so it never makes an LDS read of the other buffer wait for them;
   // the vmcnt(0) at the end of every odd slot is their only wait.
   const uint32_t lds_k_off = (uint32_t)(uintptr_t)LDS_PTR(unsigned char, &lds_k[0][0]);
@@ -408,6 +408,12 @@ void ssa_fwd_kernel(const Params p) {
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(copy_off[j] + goff), "s"(rv), "{m0}"(m0));
     else
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(copy_off[j] + goff), "s"(rk), "{m0}"(m0));
+  };
+  // The same for instruction j (0 or 1) of block blk of FP8 K tile kt.
+  auto copy_one_untracked8 = [&](int kt, uint32_t lds_tile, int blk, int j) __attribute__((always_inline)) {
+    const uint32_t goff = (uint32_t)(kt * kBK + 16 * blk) * kRow8;
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (uint32_t)((16 * blk + 8 * j) * kRow8));
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(copy_off8[j] + goff), "s"(rk8), "{m0}"(m0));
   };
 
   // Per-lane LDS byte offsets of the operand reads.
@@ -716,11 +722,11 @@ void ssa_fwd_kernel(const Params p) {
   // So on every SIMD one wave feeds the matrix cores while the other runs
   // the softmax.  The MFMA phase of tile j reads K(j) and V(j - 1) in slots
   // 2j (A) and 2j + 1 (B); group B copies K(j + 1) and V(j) into the other
-  // buffers in slot 2j (at its start in the bf16 instance with the vote, at
-  // the end of its softmax phase in the FP8 and dense ones), and every wave
-  // waits for them at the end of slot 2j + 1.  The dense instance moves the
-  // V(j) copy into group A's QK^T steps of slot 2j, so it overlaps MFMA work
-  // instead of stretching group B's softmax phase.
+  // buffers in slot 2j (at its start in the instances with the vote, at the
+  // end of its softmax phase in the dense one), and every wave waits for
+  // them at the end of slot 2j + 1.  The dense instance moves the V(j) copy
+  // into group A's QK^T steps of slot 2j, so it overlaps MFMA work instead
+  // of stretching group B's softmax phase.
   if (tid < kWaves) vote_lds[tid] = -2;
   copy_k(0, lds_k[0], wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -728,7 +734,7 @@ void ssa_fwd_kernel(const Params p) {
   const int nslots = 2 * nkt + 2;
   for (int slot = 0; slot < nslots; ++slot) {
     const int my = group_b ? slot - 1 : slot;   // this group's own slot counter
-    if constexpr (!kDense && !kFp8) {
+    if constexpr (!kDense) {
       // Group B's copies of K(j + 1) and V(j), at the start of its even slot
       // 2j, before its softmax phase.  Untracked, as in the dense instance:
       // the next slot's MFMA phase reads the other K and V buffers, so it
@@ -738,10 +744,17 @@ void ssa_fwd_kernel(const Params p) {
       if (group_b && (slot & 1) == 0) {
         const int j = slot >> 1;
         if (j + 1 < nkt) {
+          if constexpr (kFp8) {
 #pragma unroll
-          for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
-            copy_one_untracked(false, j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTileBytes),
-                               2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
+            for (int cj = 0; cj < 4; ++cj)
+              copy_one_untracked8(j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTile8Bytes),
+                                  2 * (wave - 4) + cj / 2, cj % 2);
+          } else {
+#pragma unroll
+            for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
+              copy_one_untracked(false, j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTileBytes),
+                                 2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
+          }
         }
         if (j < nkt) {
 #pragma unroll
@@ -785,23 +798,18 @@ void ssa_fwd_kernel(const Params p) {
         softmax_phase(kt);
       }
     }
-    if (group_b && (slot & 1) == 0) {
-      const int j = slot >> 1;
-      if constexpr (kDense) {
-        // V(j) was issued by group A during its QK^T steps of slot 2j
+    if constexpr (kDense) {
+      // The dense instance's K(j + 1) copy, after group B's softmax phase of
+      // slot 2j (V(j) was issued by group A during its QK^T steps); the
+      // instances with the vote issue theirs at the start of the slot.
+      if (group_b && (slot & 1) == 0) {
+        const int j = slot >> 1;
         if (j + 1 < nkt) {
 #pragma unroll
           for (int cj = 0; cj < 2 * kCopyPerWave; ++cj)
             copy_one_untracked(false, j + 1, lds_k_off + (uint32_t)(((j + 1) & 1) * kTileBytes),
                                2 * (wave - 4) + cj / kCopyPerWave, cj % kCopyPerWave);
         }
-      } else {
-        if constexpr (kFp8) {
-          if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4));
-          if (j + 1 < nkt) copy_k(j + 1, lds_k[(j + 1) & 1], 2 * (wave - 4) + 1);
-          if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4));
-          if (j < nkt) copy_block(rv, j, lds_v[j & 1], 2 * (wave - 4) + 1);
-        }   // the bf16 instance with the vote issues its copies at the start of the slot
       }
     }
     // LDS operations (votes, operand reads) complete before the barrier, so
