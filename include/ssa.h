@@ -66,7 +66,7 @@ extern "C" {
 
 typedef enum {
   SSA_OK = 0,
-  SSA_ERR_INVALID_ARG = -1,    /* null or misaligned pointer, negative size, non-finite scale */
+  SSA_ERR_INVALID_ARG = -1,    /* null or misaligned pointer, negative size, scale not finite and positive */
   SSA_ERR_UNSUPPORTED = -2,    /* head dimension other than 128, sizes beyond the grid limits */
   SSA_ERR_BAD_THRESHOLD = -3,  /* factor / threshold / lambda negative or non-finite, seqlen <= 0 */
   SSA_ERR_NO_CALIBRATION = -4, /* calibrated call with a <= 0 or non-finite a, b: use the threshold entry */

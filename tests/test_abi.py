@@ -55,6 +55,7 @@ def test_argument_errors_before_any_hip_call(lib):
     assert _fwd(lib, B=-1) == INVALID
     assert _fwd(lib, scale=float("nan")) == INVALID
     assert _fwd(lib, scale=-1.0) == INVALID
+    assert _fwd(lib, scale=0.0) == INVALID
     assert _fwd(lib, factor=-1.0) == BAD_THRESHOLD
     assert _fwd(lib, factor=float("inf")) == BAD_THRESHOLD
     assert _fwd(lib, seqlen=0) == BAD_THRESHOLD

@@ -193,6 +193,17 @@ def test_calibrated_entry(ssa):
     _run(ssa, w, "calibrated", calib=(3.0, 4.4, 0.5))
 
 
+@pytest.mark.parametrize("scale,factor", [(0.05, 2.0), (0.3, 0.02), (1.0, 1e-3)])
+def test_other_scales(ssa, scale, factor):
+    """The score scale enters the vote (tile_max = fl(raw * scale)) and the
+    exponent: scales other than 1/sqrt(128), from a flat to a steep softmax."""
+    w0 = inputs.grid_small(17, (4, 12, 20), heads=2)
+    w = inputs.Workload("grid scale", w0.q, w0.k, w0.v, scale=scale)
+    S = w.q.shape[2]
+    rep = _run(ssa, w, f"scale {scale}", factor=factor * S)
+    assert rep.skipped > 0
+
+
 def test_lambda_above_one(ssa):
     """Thresholds above 1 are accepted; later decisions depend on earlier ones."""
     w = inputs.grid_small(13, (3, 10, 13), heads=2)
