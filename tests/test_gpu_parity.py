@@ -165,6 +165,25 @@ def test_edge_lengths(ssa, S):
     _run(ssa, w, f"edge S={S}", factor=0.3 * S)
 
 
+def _sweep_case(i):
+    """Seeded case i of the shape sweep: a grid-local problem of a random
+    ragged size at a threshold from 0.05 to 10 (below and above 1)."""
+    rng = np.random.default_rng(1000 + i)
+    grid = (int(rng.integers(2, 6)), int(rng.integers(8, 25)), int(rng.integers(8, 41)))
+    w = inputs.grid_small(2000 + i, grid, heads=int(rng.integers(1, 4)))
+    return w, (0.05, 0.3, 1.0, 2.0, 5.0, 10.0)[i % 6]
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_grid_sweep(ssa, i):
+    """Sixteen seeded grid-local problems of random ragged sizes (about 300
+    to 5,000 tokens, 1 to 3 heads) at thresholds below and above 1."""
+    w, lam = _sweep_case(i)
+    S = w.q.shape[2]
+    rep = _run(ssa, w, f"sweep {i} S={S} lambda={lam:.4g}", threshold=lam)
+    assert rep.tiles > 0
+
+
 def test_many_heads_small(ssa):
     w = inputs.random_qkv(7, 3, 17, 200, qk_gain=2.0)
     _run(ssa, w, "B3H17", factor=0.0)
