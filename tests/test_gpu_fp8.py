@@ -300,3 +300,12 @@ def test_fp8_edge_lengths(ssa, S):
     """Shorter than a query block, one key past a tile, ragged in both."""
     w = inputs.random_qkv(200 + S, 2, 3, S, qk_gain=2.0)
     _check_attention(ssa, w, f"fp8 edge S={S}", factor=0.3 * S)
+
+
+@pytest.mark.parametrize("i", range(0, 16, 2))
+def test_random_grid_sweep(ssa, i):
+    """Every other case of the plain path's seeded shape sweep (ragged
+    grid-local problems at thresholds 0.05 to 10) on the FP8 entry."""
+    from tests.test_gpu_parity import _sweep_case
+    w, lam = _sweep_case(i)
+    _check_attention(ssa, w, f"fp8 sweep {i} S={w.q.shape[2]} lambda={lam:.4g}", threshold=lam)
