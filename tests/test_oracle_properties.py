@@ -13,6 +13,7 @@ thresholds drawn at random.
 import math
 
 import numpy as np
+import torch
 from hypothesis import HealthCheck, given, settings
 from hypothesis import strategies as st
 
@@ -33,7 +34,7 @@ def problems(draw):
     rng = np.random.default_rng(seed)
     # bf16-representable values, so that every score is exact in float64
     def bf(x):
-        return oracle.from_bf16(__import__("torch").from_numpy(x.astype(np.float32)).bfloat16())
+        return oracle.from_bf16(torch.from_numpy(x.astype(np.float32)).bfloat16())
     q, k, v = (bf(gain * rng.standard_normal((S, D))) for _ in range(3))
     scale = draw(st.sampled_from([0.25, 0.7, 1.0]))
     return q, k, v, scale, bq, bk
